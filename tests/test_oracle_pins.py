@@ -1,0 +1,543 @@
+"""Pins of the CPU oracle to things other than itself (closed forms, brute force, textbook
+routines, invariants and the pages' tables).  CPU only.
+
+Each test names the oracle function it pins and the kind of mistake it is there to catch.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from oracle import OracleParams
+from oracle.fadkv_oracle import (FLAG_EXHAUSTED, FLAG_NONFINITE, FLAG_REPLACED, FLAG_TRIGGER,
+                                 _round_bf16)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def unit_rows(a):
+    return a / np.linalg.norm(a, axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------------------
+# storage rounding: brute force over every representable value of the format
+# ---------------------------------------------------------------------------------------
+
+def _all_values(bits_to_f64, count):
+    vals = bits_to_f64(np.arange(count, dtype=np.uint32))
+    fin = np.isfinite(vals)
+    pats = np.arange(count, dtype=np.uint32)[fin]
+    vals = vals[fin]
+    order = np.argsort(vals, kind="stable")
+    vals, pats = vals[order], pats[order]
+    keep = np.concatenate([[True], np.diff(vals) != 0])   # drop -0 duplicate of +0
+    return vals[keep], pats[keep]
+
+
+def _nearest_even(v, vals, pats):
+    i = np.searchsorted(vals, v)
+    lo, hi = vals[max(i - 1, 0)], vals[min(i, len(vals) - 1)]
+    if v == hi:
+        return hi
+    dl, dh = v - lo, hi - v
+    if dl < dh:
+        return lo
+    if dh < dl:
+        return hi
+    plo, phi = pats[max(i - 1, 0)], pats[min(i, len(vals) - 1)]
+    return lo if (plo & 1) == 0 else hi
+
+
+def _probe_values(rng, scale):
+    v = rng.standard_normal(3000) * scale
+    # exact midpoints between neighbours exercise ties-to-even
+    return v
+
+
+def test_bf16_rounding_is_nearest_even_bruteforce():
+    """pins round_to_storage('bf16'): wrong shift, truncation or ties-away fail here."""
+    with np.errstate(invalid="ignore"):
+        vals, pats = _all_values(
+            lambda b: ((b << 16).astype(np.uint32)).view(np.float32).astype(np.float64), 1 << 16)
+    rng = np.random.default_rng(1)
+    probes = list(_probe_values(rng, 1.0)) + list(_probe_values(rng, 1e-38)) + [
+        1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -133 * 1.5,
+        2.0 ** -134, 3.0 * 2.0 ** -134]
+    for v in probes:
+        assert _round_bf16(np.array([v]))[0] == _nearest_even(v, vals, pats), v
+
+
+def test_f16_rounding_is_nearest_even_bruteforce():
+    """pins round_to_storage('f16') (NumPy's float64 -> float16) against brute force."""
+    vals, pats = _all_values(
+        lambda b: b.astype(np.uint16).view(np.float16).astype(np.float64), 1 << 16)
+    rng = np.random.default_rng(2)
+    probes = list(_probe_values(rng, 1.0)) + list(_probe_values(rng, 1e-6)) + [
+        1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -25, 3 * 2.0 ** -26]
+    for v in probes:
+        assert oracle.round_to_storage(np.array([v]), "f16")[0] == _nearest_even(v, vals, pats)
+
+
+# ---------------------------------------------------------------------------------------
+# a1 screening scores
+# ---------------------------------------------------------------------------------------
+
+def test_scores_identity_dictionary_returns_x():
+    """pins screening_scores: with D = I the scores are x itself."""
+    x = np.random.default_rng(0).standard_normal(16)
+    np.testing.assert_array_equal(oracle.screening_scores(np.eye(16), x), x)
+
+
+def test_scores_match_python_loops():
+    """pins screening_scores: a transposed operand or wrong axis fails on a non-square D."""
+    rng = np.random.default_rng(3)
+    D = rng.standard_normal((7, 5))
+    x = rng.standard_normal(5)
+    ref = [sum(D[j][i] * x[i] for i in range(5)) for j in range(7)]
+    np.testing.assert_allclose(oracle.screening_scores(D, x), ref, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------
+# a2 pool
+# ---------------------------------------------------------------------------------------
+
+def test_pool_matches_python_sort():
+    """pins candidate_pool: ranking by |sigma| (not sigma) then lowest index."""
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        N, n = 40, 9
+        sig = np.round(rng.standard_normal(N), 1)   # coarse values -> many exact ties
+        P, _ = oracle.candidate_pool(sig, n)
+        ref = sorted(range(N), key=lambda j: (-abs(sig[j]), j))[:n]
+        assert list(P) == ref
+
+
+def test_pool_ties_go_to_lowest_index():
+    sig = np.array([0.5, -2.0, 1.0, 2.0, -1.0, 1.0])
+    P, near = oracle.candidate_pool(sig, 3)
+    assert list(P) == [1, 3, 2]
+    assert near  # 1.0 (index 2) vs 1.0 (index 4) at the boundary
+
+
+def test_pool_with_n_equal_N_is_everything():
+    sig = np.random.default_rng(5).standard_normal(12)
+    P, near = oracle.candidate_pool(sig, 12)
+    assert sorted(P) == list(range(12)) and not near
+
+
+def test_pool_near_tie_flag_threshold():
+    sig = np.array([1.0, 0.5, 0.5 * (1 - 0.5e-5), 0.1])
+    assert oracle.candidate_pool(sig, 2)[1]
+    sig = np.array([1.0, 0.5, 0.5 * (1 - 2e-5), 0.1])
+    assert not oracle.candidate_pool(sig, 2)[1]
+
+
+# ---------------------------------------------------------------------------------------
+# a4 ridge
+# ---------------------------------------------------------------------------------------
+
+def test_ridge_normal_equations_and_cholesky():
+    """pins ridge_coefficients: residual of the normal equations and scipy's cho_solve."""
+    rng = np.random.default_rng(6)
+    for s in (1, 3, 8, 16):
+        D_S = unit_rows(rng.standard_normal((s, 32))) * rng.uniform(0.5, 2, (s, 1))
+        b = rng.standard_normal(s)
+        c = oracle.ridge_coefficients(D_S, b, 1e-4, 0.2)
+        G = D_S @ D_S.T
+        A = G + np.diag(1e-4 + 0.2 * np.diag(G))
+        assert np.linalg.norm(A @ c - b) <= 1e-12 * np.linalg.norm(b)
+        np.testing.assert_allclose(c, scipy.linalg.cho_solve(scipy.linalg.cho_factor(A), b),
+                                   rtol=1e-11, atol=1e-13)
+
+
+def test_ridge_system_diagonal_is_1p2_G_plus_1em4():
+    """pins ridge_system against Table 5's lambda with non-unit diagonal (catches abs/rel swaps
+    and a lambda that ignores diag(G))."""
+    G = np.array([[4.0, 1.0], [1.0, 9.0]])
+    A = oracle.ridge_system(G, 1e-4, 0.2)
+    np.testing.assert_allclose(A, np.array([[4.8001, 1.0], [1.0, 10.8001]]), rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------------------
+# a3 GM / PL
+# ---------------------------------------------------------------------------------------
+
+def test_gm_s1_closed_form():
+    """s = 1: S = argmax|sigma| and c = sigma_j / (1.2 G_jj + 1e-4), with non-unit atoms."""
+    rng = np.random.default_rng(7)
+    D = unit_rows(rng.standard_normal((30, 12))) * rng.uniform(0.5, 3.0, (30, 1))
+    x = rng.standard_normal(12)
+    p = OracleParams(n=10, s=1)
+    vc = oracle.encode_vector(D, x, p, 0.5)
+    sig = D @ x
+    j = int(np.argmax(np.abs(sig)))
+    assert vc.idx[0] == j
+    g = D[j] @ D[j]
+    assert vc.coef[0] == pytest.approx(sig[j] / (1.2 * g + 1e-4), rel=1e-13)
+    e = np.linalg.norm(x - vc.coef[0] * D[j]) / np.linalg.norm(x)
+    assert vc.relerr == pytest.approx(e, rel=1e-13)
+
+
+def test_gm_ties_go_to_lowest_index():
+    """Two identical atoms (indices 1 and 3) tie exactly at the first greedy step: the lower
+    index is taken, and its duplicate is then passed over for the next-best atom."""
+    D = np.array([[0.0, 1, 0], [1, 0, 0], [0, 0, 1], [1, 0, 0]])
+    x = np.array([1.0, 0.5, 0.0])
+    gm = oracle.encode_vector(D, x, OracleParams(n=4, s=2), 0.5)
+    assert list(gm.idx) == [1, 0]      # rho_3 = 1 - 1/1.2001 < rho_0 = 0.5
+    assert gm.ties & oracle.fadkv_oracle.TIE_GREEDY
+    # PL ranks by |sigma| alone: both duplicates, lower index first
+    pl = oracle.encode_vector(D, x, OracleParams(n=4, s=2, select="pl"), 0.5)
+    assert list(pl.idx) == [1, 3]
+
+
+def test_gm_orthonormal_closed_form():
+    """Orthonormal D (G = I): S = the s largest |sigma| in order, c = sigma_S / 1.2001 and
+    e^2 = (||x||^2 - ||sigma_S||^2 + (0.2001/1.2001)^2 ||sigma_S||^2) / ||x||^2."""
+    rng = np.random.default_rng(8)
+    d = 24
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    for s, n in ((4, 10), (6, 24), (3, 3)):
+        x = rng.standard_normal(d)
+        vc = oracle.encode_vector(Q, x, OracleParams(n=n, s=s), 0.5)
+        sig = Q @ x
+        ref = list(np.argsort(-np.abs(sig), kind="stable")[:s])
+        assert list(vc.idx) == ref
+        np.testing.assert_allclose(vc.coef, sig[ref] / 1.2001, rtol=1e-12)
+        ss = np.sum(sig[ref] ** 2)
+        e2 = (x @ x - ss + (0.2001 / 1.2001) ** 2 * ss) / (x @ x)
+        assert vc.relerr == pytest.approx(np.sqrt(e2), rel=1e-12)
+
+
+def test_gm_with_full_pool_and_no_ridge_is_textbook_omp():
+    """n = N and lambda = 0 reduce GM to OMP: supports (as sets) and least-squares coefficients
+    match scikit-learn's orthogonal_mp.  Catches sign or index mistakes in the rho update."""
+    from sklearn.linear_model import orthogonal_mp
+    rng = np.random.default_rng(9)
+    checked = 0
+    for trial in range(40):
+        N, d, s = 60, 20, 5
+        D = unit_rows(rng.standard_normal((N, d)))
+        x = rng.standard_normal(d)
+        p = OracleParams(n=N, s=s, ridge_abs=0.0, ridge_rel=0.0)
+        vc = oracle.encode_vector(D, x, p, 0.5)
+        if vc.ties:
+            continue
+        ref = orthogonal_mp(D.T, x, n_nonzero_coefs=s)
+        assert set(np.flatnonzero(ref)) == set(vc.idx.tolist())
+        np.testing.assert_allclose(ref[vc.idx], vc.coef, rtol=1e-8, atol=1e-10)
+        checked += 1
+    assert checked >= 30
+
+
+def _low_coherence_dictionary():
+    H = scipy.linalg.hadamard(16) / 4.0
+    return np.vstack([np.eye(16), H])      # 32 unit atoms, mutual coherence 1/4
+
+
+def test_gm_exact_recovery_and_best_subset_low_coherence():
+    """Mutual coherence 1/4 < 1/(2s-1) for s = 2: greedy pursuit must recover every planted
+    2-sparse vector, and brute force over all C(32,2) subsets finds the same unique
+    zero-error support (lambda = 0, n = N)."""
+    D = _low_coherence_dictionary()
+    N = D.shape[0]
+    rng = np.random.default_rng(10)
+    p = OracleParams(n=N, s=2, ridge_abs=0.0, ridge_rel=0.0)
+    for _ in range(60):
+        S = rng.choice(N, 2, replace=False)
+        a = rng.uniform(0.5, 2.0, 2) * rng.choice([-1, 1], 2)
+        x = a @ D[S]
+        vc = oracle.encode_vector(D, x, p, 0.5)
+        assert set(vc.idx.tolist()) == set(S.tolist())
+        assert vc.relerr < 1e-12
+        best = min(itertools.combinations(range(N), 2),
+                   key=lambda T: np.linalg.norm(
+                       x - D[list(T)].T @ np.linalg.lstsq(D[list(T)].T, x, rcond=None)[0]))
+        assert set(best) == set(S.tolist())
+
+
+def test_gm_best_subset_on_tiny_random_dictionaries():
+    """Brute force best-s-subset (N = 24, d = 16, s <= 3) on planted noise-free vectors with
+    |a| in [0.5, 2]: the planted support is the unique zero-error subset; where GM (full pool,
+    lambda = 0) reaches zero error its support must be that subset."""
+    rng = np.random.default_rng(11)
+    agree = total = 0
+    for trial in range(30):
+        s = 1 + trial % 3
+        D = unit_rows(rng.standard_normal((24, 16)))
+        S = rng.choice(24, s, replace=False)
+        a = rng.uniform(0.5, 2.0, s) * rng.choice([-1, 1], s)
+        x = a @ D[S]
+        errs = {}
+        for T in itertools.combinations(range(24), s):
+            DT = D[list(T)].T
+            r = x - DT @ np.linalg.lstsq(DT, x, rcond=None)[0]
+            errs[T] = np.linalg.norm(r) / np.linalg.norm(x)
+        best = min(errs, key=errs.get)
+        assert set(best) == set(S.tolist()) and errs[best] < 1e-12
+        vc = oracle.encode_vector(D, x, OracleParams(n=24, s=s, ridge_abs=0.0, ridge_rel=0.0), 0.5)
+        if vc.relerr < 1e-10:
+            assert set(vc.idx.tolist()) == set(S.tolist())
+            agree += 1
+        total += 1
+    assert agree >= total // 2
+
+
+def test_gm_planted_recovery_tiny_workload_shape():
+    """Tiny-workload shape (N=256, d=64, s=4), noise-free planted vectors with |a_i| in
+    [0.3, 1.3]: with the whole dictionary as pool the greedy recovers every planted support,
+    and at n = 32 it recovers every vector whose planted atoms all made the pool (a missed
+    recovery then can only come from the screening, not from the greedy or the ridge)."""
+    rng = np.random.default_rng(12)
+    D = unit_rows(rng.standard_normal((256, 64)))
+    in_pool = 0
+    for _ in range(200):
+        S = rng.choice(256, 4, replace=False)
+        a = rng.uniform(0.3, 1.3, 4) * rng.choice([-1, 1], 4)
+        x = a @ D[S]
+        full = oracle.encode_vector(D, x, OracleParams(n=256, s=4), 0.5)
+        assert set(full.idx.tolist()) == set(S.tolist())
+        P, _ = oracle.candidate_pool(D @ x, 32)
+        if set(S.tolist()) <= set(P.tolist()):
+            vc = oracle.encode_vector(D, x, OracleParams(n=32, s=4), 0.5)
+            assert set(vc.idx.tolist()) == set(S.tolist())
+            in_pool += 1
+    assert in_pool >= 120
+
+
+def test_pl_takes_the_s_largest_of_the_pool():
+    rng = np.random.default_rng(13)
+    D = unit_rows(rng.standard_normal((50, 10)))
+    x = rng.standard_normal(10)
+    p = OracleParams(n=20, s=5, select="pl")
+    vc = oracle.encode_vector(D, x, p, 0.5)
+    sig = D @ x
+    ref = sorted(range(50), key=lambda j: (-abs(sig[j]), j))[:5]
+    assert list(vc.idx) == ref
+    np.testing.assert_allclose(vc.coef, oracle.ridge_coefficients(D[ref], sig[ref], 1e-4, 0.2),
+                               rtol=1e-13)
+
+
+def test_pl_equals_gm_on_orthonormal_dictionary():
+    rng = np.random.default_rng(14)
+    Q, _ = np.linalg.qr(rng.standard_normal((16, 16)))
+    x = rng.standard_normal(16)
+    a = oracle.encode_vector(Q, x, OracleParams(n=8, s=4, select="pl"), 0.5)
+    b = oracle.encode_vector(Q, x, OracleParams(n=8, s=4, select="gm"), 0.5)
+    assert list(a.idx) == list(b.idx)
+    np.testing.assert_allclose(a.coef, b.coef, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# a5 residual, reconstruct, special inputs
+# ---------------------------------------------------------------------------------------
+
+def test_relerr_agrees_with_reconstruct():
+    rng = np.random.default_rng(15)
+    D = unit_rows(rng.standard_normal((64, 16)))
+    X = rng.standard_normal((1, 20, 16))
+    p = OracleParams(n=16, s=3)
+    codes = oracle.encode(D[None], X, p)
+    xh = oracle.reconstruct(D[None], codes.idx, codes.coef)
+    e = np.linalg.norm(X - xh, axis=2) / np.linalg.norm(X, axis=2)
+    np.testing.assert_allclose(codes.relerr, e, rtol=1e-12)
+
+
+def test_reconstruct_by_hand():
+    D = np.arange(12, dtype=np.float64).reshape(1, 4, 3)
+    idx = np.array([[[2, 0, -1]]], dtype=np.int32)
+    coef = np.array([[[0.5, -1.0, 7.0]]])
+    np.testing.assert_array_equal(oracle.reconstruct(D, idx, coef)[0, 0],
+                                  0.5 * np.array([6, 7, 8.0]) - np.array([0, 1, 2.0]))
+
+
+def test_zero_and_nonfinite_vectors():
+    D = unit_rows(np.random.default_rng(16).standard_normal((20, 8)))
+    p = OracleParams(n=5, s=2)
+    z = oracle.encode_vector(D, np.zeros(8), p, 0.5)
+    assert list(z.idx) == [-1, -1] and z.relerr == 0.0 and z.flags == 0
+    x = np.ones(8)
+    x[3] = np.nan
+    nf = oracle.encode_vector(D, x, p, 0.5)
+    assert list(nf.idx) == [-1, -1] and np.isnan(nf.relerr) and nf.flags == FLAG_NONFINITE
+
+
+def test_delta_by_dictionary_parity_and_strict_threshold():
+    """Keys (even dictionaries) use 0.50, values (odd) 0.70; trigger is e > delta."""
+    p = OracleParams()
+    assert p.delta(0) == 0.5 and p.delta(1) == 0.7 and p.delta(54) == 0.5 and p.delta(55) == 0.7
+    Q = np.eye(4)
+    x = np.array([1.0, 0.0, 0.0, 0.0])
+    # one atom equal to x: e = 0.2001/1.2001 exactly representable check of strictness
+    vc = oracle.encode_vector(Q, x, OracleParams(n=2, s=1), 0.2001 / 1.2001)
+    assert not (vc.flags & FLAG_TRIGGER)
+
+
+# ---------------------------------------------------------------------------------------
+# a6 adaptation invariants
+# ---------------------------------------------------------------------------------------
+
+def _adapt_run(steps=8, rows=64, tau_c=1, seed=20, N=256, d=64, s=4, n=32, drift=0.2,
+               support_limit=192):
+    rng = np.random.default_rng(seed)
+    atoms = oracle.round_to_storage(unit_rows(rng.standard_normal((1, N, d))[0]), "f32")[None]
+    usage = np.zeros((1, N), dtype=np.int64)
+    p = OracleParams(n=n, s=s, tau_c=tau_c)
+    history = []
+    for step in range(steps):
+        X = np.empty((1, rows, d))
+        for m in range(rows):
+            if rng.uniform() < drift:
+                X[0, m] = rng.standard_normal(d)
+            else:
+                S = rng.choice(support_limit, s, replace=False)
+                X[0, m] = rng.standard_normal(s) @ atoms[0, S]
+        X = oracle.round_to_storage(X, "f32")
+        codes = oracle.encode(atoms, X, p)
+        new_atoms, new_usage, new_codes, replaced = oracle.adapt(atoms, usage, X, codes, p, "f32")
+        history.append((atoms, usage, X, codes, new_atoms, new_usage, new_codes, replaced))
+        atoms, usage = new_atoms, new_usage
+    return p, history
+
+
+def test_adapt_keeps_size_and_counts_usage():
+    p, hist = _adapt_run()
+    committed = 0
+    replaced_total = 0
+    for atoms, usage, X, codes, na, nu, nc, rep in hist:
+        assert na.shape == atoms.shape and nu.shape == usage.shape   # N never changes
+        committed += int(np.sum(nc.idx >= 0))
+        assert int(nu.sum()) == committed                             # sum usage = slots
+        replaced_total += int(np.sum(rep >= 0))
+    assert replaced_total > 0
+
+
+def test_adapt_replaced_atom_and_code():
+    p, hist = _adapt_run()
+    seen = 0
+    for atoms, usage, X, codes, na, nu, nc, rep in hist:
+        for m in np.flatnonzero(rep[0] >= 0):
+            j = rep[0, m]
+            x = X[0, m]
+            a = oracle.round_to_storage(x / np.linalg.norm(x), "f32")
+            np.testing.assert_array_equal(na[0, j], a)
+            assert nu[0, j] == 1 and usage[0, j] < p.tau_c
+            assert nc.idx[0, m, 0] == j and np.all(nc.idx[0, m, 1:] == -1)
+            g = a @ a
+            assert nc.coef[0, m, 0] == pytest.approx((a @ x) / (1.2 * g + 1e-4), rel=1e-13)
+            assert nc.relerr[0, m] == pytest.approx(0.2001 / 1.2001, rel=1e-5)
+            assert nc.flags[0, m] & FLAG_REPLACED and nc.flags[0, m] & FLAG_TRIGGER
+            seen += 1
+    assert seen > 0
+
+
+def test_adapt_never_overwrites_a_referenced_atom():
+    """With tau_c = 1 no committed code of any step references an atom overwritten later."""
+    p, hist = _adapt_run(steps=10)
+    live = set()   # atoms referenced by committed codes so far
+    for atoms, usage, X, codes, na, nu, nc, rep in hist:
+        step_sel = set(int(j) for j in codes.idx[0].ravel() if j >= 0)
+        for j in rep[0][rep[0] >= 0]:
+            assert int(j) not in live and int(j) not in step_sel
+        live |= set(int(j) for j in nc.idx[0].ravel() if j >= 0)
+        # untouched atoms keep their values bit for bit
+        mask = np.ones(atoms.shape[1], bool)
+        mask[rep[0][rep[0] >= 0]] = False
+        np.testing.assert_array_equal(atoms[0, mask], na[0, mask])
+
+
+def test_adapt_swapping_two_triggering_rows_swaps_their_slots():
+    """Slots are handed out in row order: after swapping two triggering rows, each vector
+    lands in the other's slot, so the two written atoms trade contents and nothing else moves."""
+    p, hist = _adapt_run(steps=1)
+    atoms, usage, X, codes, na, nu, nc, rep = hist[0]
+    trig = np.flatnonzero(codes.flags[0] & FLAG_TRIGGER)
+    assert trig.size >= 2
+    a, b = trig[0], trig[-1]
+    ja, jb = rep[0, a], rep[0, b]
+    assert ja >= 0 and jb >= 0 and ja != jb
+    perm = np.arange(X.shape[1])
+    perm[a], perm[b] = b, a
+    codes2 = oracle.Codes(codes.idx[:, perm], codes.coef[:, perm], codes.relerr[:, perm],
+                          codes.flags[:, perm], codes.ties[:, perm])
+    na2, nu2, _, rep2 = oracle.adapt(atoms, usage, X[:, perm], codes2, p, "f32")
+    np.testing.assert_array_equal(rep2, rep)
+    np.testing.assert_array_equal(na2[0, ja], na[0, jb])
+    np.testing.assert_array_equal(na2[0, jb], na[0, ja])
+    rest = np.ones(atoms.shape[1], bool)
+    rest[[ja, jb]] = False
+    np.testing.assert_array_equal(na2[0, rest], na[0, rest])
+    np.testing.assert_array_equal(nu2, nu)
+
+
+def test_adapt_candidates_ordered_by_usage_then_index():
+    """tau_c = 3, preset usage: candidates are taken in (usage, index) order, skipping atoms
+    with usage >= tau_c and atoms selected by this step's codes."""
+    N, d = 8, 4
+    A = np.vstack([np.eye(4), -np.eye(4)])[None]
+    usage = np.array([[2, 0, 5, 1, 0, 2, 1, 3]])
+    X = np.ones((1, 4, d))
+    X[0, :, 0] = [1, 2, 3, 4]
+    idx = np.full((1, 4, 1), -1, np.int32)
+    idx[0, 2, 0] = 4          # a triggering row whose code uses atom 4 protects it
+    codes = oracle.Codes(idx, np.zeros((1, 4, 1)), np.ones((1, 4)),
+                         np.full((1, 4), FLAG_TRIGGER, np.uint8), np.zeros((1, 4), np.uint8))
+    p = OracleParams(n=1, s=1, tau_c=3)
+    _, nu, nc, rep = oracle.adapt(A, usage, X, codes, p, "f32")
+    # eligible: usage<3 and not atom 4 -> {1:0, 3:1, 6:1, 0:2, 5:2}; order 1,3,6,0 for 4 rows
+    assert list(rep[0]) == [1, 3, 6, 0]
+
+
+def test_adapt_exhaustion_when_no_inactive_atom():
+    p, hist = _adapt_run(steps=1)
+    atoms, usage, X, codes, *_ = hist[0]
+    full = np.full_like(usage, p.tau_c)
+    na, nu, nc, rep = oracle.adapt(atoms, full, X, codes, p, "f32")
+    trig = (codes.flags[0] & FLAG_TRIGGER) != 0
+    assert trig.any()
+    assert np.all(rep == -1)
+    assert np.all((nc.flags[0][trig] & FLAG_EXHAUSTED) != 0)
+    np.testing.assert_array_equal(na, atoms)
+    assert int(nu.sum() - full.sum()) == int(np.sum(codes.idx >= 0))
+
+
+def test_adapt_delta_extremes():
+    rng = np.random.default_rng(21)
+    D = unit_rows(rng.standard_normal((1, 64, 16)))
+    X = rng.standard_normal((1, 10, 16))
+    X[0, 3] = 0.0
+    lo = oracle.encode(D, X, OracleParams(n=8, s=2, delta_key=0.0))
+    hi = oracle.encode(D, X, OracleParams(n=8, s=2, delta_key=np.inf))
+    assert (lo.flags[0] & FLAG_TRIGGER).sum() == 9          # every non-zero row
+    assert (hi.flags[0] & FLAG_TRIGGER).sum() == 0
+
+
+# ---------------------------------------------------------------------------------------
+# the pages' tables
+# ---------------------------------------------------------------------------------------
+
+def test_cost_model_reproduces_table4_cost_column():
+    """Reading of GM/PL: screening costs N*d MACs per vector, GM's greedy s*n*d, PL's solve
+    s*s*d; against full OMP (s*N*d) this gives Table 4's 0.19 and 0.13 at N=4096, s=8, n=256."""
+    g = json.load(open(os.path.join(GOLDEN, "table4_efficiency.json")))
+    N, s, n = g["model_shape"]["N"], g["model_shape"]["s"], g["model_shape"]["n"]
+    gm = (N + s * n) / (s * N)
+    pl = (N + s * s) / (s * N)
+    assert round(gm, 2) == g["rows"]["GM (ours)"][0] == g["rows"]["FAD-KV (GM)"][0]
+    assert round(pl, 2) == g["rows"]["PL (ours)"][0]
+    for name, row in g["rows"].items():
+        assert row[2] == pytest.approx(1000.0 / row[1], abs=0.01)     # tok/s = 1000 / ms
+        if row[3] is not None:
+            assert row[3] == pytest.approx(53.63 / row[1] - 1, abs=0.0006)
+
+
+def test_table5_defaults():
+    g = json.load(open(os.path.join(GOLDEN, "table5_hyperparameters.json")))
+    p = OracleParams()
+    assert (p.n, p.s) == (g["by_model_size"]["3B"]["n"], g["by_model_size"]["3B"]["s"])
+    assert p.ridge_abs == g["ridge"]["abs"] and p.ridge_rel == g["ridge"]["rel_diag_G"]
+    assert p.delta_key == g["delta"]["key"] and p.delta_value == g["delta"]["value"]
