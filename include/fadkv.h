@@ -1,0 +1,156 @@
+/*
+ * fadkv.h -- C ABI of the FAD-KV screening sparse coder with fixed-size dictionary
+ * adaptation, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "FAD-KV: Adaptive Dictionary KV Caching for Efficient Reasoning
+ * Decoding" (arXiv 2610.37921):
+ *   - fadkv_encode: abstract and Figure 1 -- each key/value head vector x is screened against
+ *     every atom of its dictionary (scores sigma_j = <d_j, x>), a Top-n pool of the largest
+ *     |sigma| is kept, s atoms are chosen inside the pool ("GM" greedy pursuit, or "PL" the s
+ *     largest scores; Tables 1-4), and coefficients come from the ridge system of Table 5,
+ *     (G_SS + diag(ridge_abs + ridge_rel * G_jj)) c = D_S x.  The relative residual
+ *     ||x - D_S^T c|| / ||x|| is compared with delta (Table 5: 0.50 keys, 0.70 values).
+ *   - fadkv_adapt: Figure 2 -- vectors whose error exceeds delta overwrite an inactive atom
+ *     with their own direction instead of growing the dictionary, so N never changes.
+ *   - fadkv_reconstruct: the stored sparse code turned back into a vector (abstract).
+ *
+ * Conventions shared by every call
+ *   - Layout.  A "dictionary set" holds num_dicts independent dictionaries; dictionary t of a
+ *     model is 2*layer + 0 for keys and 2*layer + 1 for values (delta is chosen by parity).
+ *     atoms are row-major [num_dicts][N][d]; vectors X are [num_dicts][M][d] with the rows of
+ *     each dictionary in (head, sequence, token) order -- that order is the commit order of
+ *     fadkv_adapt.  Codes are [num_dicts][M][s] (idx int32, coef float) plus relerr float and
+ *     flags uint8 per vector.  All these are DEVICE pointers, caller-owned; the library keeps
+ *     no pointer after a call returns.
+ *   - dtypes.  atoms and X share one storage dtype: FADKV_F32, FADKV_F16 or FADKV_BF16.
+ *     Scores multiply in that dtype and accumulate in fp32; everything after the screening
+ *     (pool scores, Cholesky, residual) is fp32; new atoms are normalised in fp64 and rounded
+ *     to the storage dtype (round to nearest even).
+ *   - Limits.  d in {64, 128}; 1 <= N <= 65535; 1 <= s <= n <= min(N, 512); s <= 32;
+ *     1 <= num_dicts; 0 <= M and num_dicts * M < 2^31.  atoms, X and X_hat must be 16-byte
+ *     aligned, the other arrays 4-byte aligned (flags: any alignment).
+ *   - Streams.  Every call only enqueues work on `stream` (0 = the null stream) and never
+ *     synchronises.  On one stream, encode of step t+1 sees adapt of step t.  Calls are
+ *     capturable into HIP graphs (no memset or allocation is enqueued).
+ *   - Memory.  The calls allocate nothing.  Scratch space is the caller's `workspace`, sized
+ *     by fadkv_workspace_bytes; one workspace may be reused by consecutive calls on one stream.
+ *   - Errors.  Arguments are checked on the host before anything is enqueued; a bad argument
+ *     returns a negative fadkv_status and launches nothing.  A failed launch returns
+ *     FADKV_ERR_HIP.  Per-vector outcomes (trigger, replacement, exhaustion, non-finite
+ *     input) are reported in flags, never as a status.
+ *   - Threads.  Calls on disjoint buffers may run concurrently from several host threads.
+ */
+#ifndef FADKV_H
+#define FADKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FADKV_ABI_VERSION 1
+
+typedef enum {
+  FADKV_OK = 0,
+  FADKV_ERR_ARG = -1,       /* null or misaligned pointer, negative count, bad parameter */
+  FADKV_ERR_DTYPE = -2,     /* unsupported dtype code */
+  FADKV_ERR_SHAPE = -3,     /* d, N, n, s or M outside the limits above */
+  FADKV_ERR_WORKSPACE = -4, /* workspace null or smaller than fadkv_workspace_bytes */
+  FADKV_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed */
+} fadkv_status;
+
+typedef enum { FADKV_F32 = 0, FADKV_F16 = 1, FADKV_BF16 = 2 } fadkv_dtype;
+
+/* Support rule inside the pool (Tables 1-4 name both; the pages do not define them):
+ * GM = s greedy steps, each taking the pool atom of largest |sigma_j - sum_m G_jm c_m|
+ *      (ties to the lowest atom index) and re-solving the ridge system;
+ * PL = the s pool atoms of largest |sigma| (ties to the lowest index), one ridge solve. */
+typedef enum { FADKV_SELECT_GM = 0, FADKV_SELECT_PL = 1 } fadkv_select;
+
+/* flags byte per vector */
+#define FADKV_FLAG_TRIGGER 0x01u   /* relative error > delta                          */
+#define FADKV_FLAG_REPLACED 0x02u  /* adapt wrote this vector's direction into an atom */
+#define FADKV_FLAG_EXHAUSTED 0x04u /* triggered but no inactive atom was left          */
+#define FADKV_FLAG_NONFINITE 0x08u /* input held NaN/Inf: empty code, relerr = NaN     */
+
+typedef struct {
+  int32_t num_dicts; /* independent dictionaries in the set                       */
+  int32_t N;         /* atoms per dictionary (fixed for the life of the set)      */
+  int32_t d;         /* head_dim                                                   */
+  int32_t dtype;     /* fadkv_dtype of atoms (and of X)                            */
+  void *atoms;       /* device [num_dicts][N][d]; only fadkv_adapt writes it       */
+  uint32_t *usage;   /* device [num_dicts][N]; committed codes per atom; only
+                        fadkv_adapt writes it (start from zeros)                   */
+} fadkv_dict;
+
+typedef struct {
+  int32_t n;         /* candidate-pool size (Table 5: 256, or 512 for 8B models)   */
+  int32_t s;         /* sparsity (Table 5: 8, or 16 for 8B models)                  */
+  float ridge_abs;   /* Table 5: 1e-4                                              */
+  float ridge_rel;   /* Table 5: 0.20                                              */
+  float delta_key;   /* Table 5: 0.50, used by even dictionaries                    */
+  float delta_value; /* Table 5: 0.70, used by odd dictionaries                     */
+  uint32_t tau_c;    /* atom inactive iff usage < tau_c (and unselected this step);
+                        1 = never referenced by a committed code                    */
+  int32_t select;    /* fadkv_select                                               */
+} fadkv_params;
+
+typedef struct {
+  int32_t *idx;   /* device [num_dicts][M][s]: atom indices in selection order, -1 = empty */
+  float *coef;    /* device [num_dicts][M][s]: coefficients, 0 for empty slots             */
+  float *relerr;  /* device [num_dicts][M]: ||x - x_hat|| / ||x|| (0 for x = 0)            */
+  uint8_t *flags; /* device [num_dicts][M]: FADKV_FLAG_* bits                              */
+} fadkv_codes;
+
+/* Bytes of device workspace that fadkv_encode and fadkv_adapt need for M vectors per
+ * dictionary (the larger of the two; one buffer serves both).  Writes *bytes and returns
+ * FADKV_OK, or a negative status if the shapes are outside the limits. */
+int fadkv_workspace_bytes(const fadkv_dict *dict, const fadkv_params *params, int64_t M,
+                          size_t *bytes);
+
+/* Encode M vectors per dictionary (abstract; Figure 1; Table 5).
+ *   X: device [num_dicts][M][d] in dict->dtype.
+ *   out: codes written for every vector; flags get TRIGGER or NONFINITE only.
+ * A vector of zeros gets the empty code and relerr 0.  The dictionary is read only. */
+int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
+                 const fadkv_codes *out, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Commit one step's codes and apply fixed-size adaptation (Figure 2), per dictionary:
+ *   1. usage[j] += 1 for every atom of every non-triggering code;
+ *   2. candidates = atoms with usage < tau_c that no code of this step selected, ordered by
+ *      (usage, atom index);
+ *   3. the k-th triggering row (row order) takes the k-th candidate j: atom j becomes
+ *      x/||x|| rounded to the storage dtype, usage[j] = 1, and the row's code becomes the
+ *      single atom j with coefficient <d_j, x> / ((1 + ridge_rel) ||d_j||^2 + ridge_abs)
+ *      (relerr recomputed, flag REPLACED);
+ *   4. triggering rows beyond the candidates keep their code, commit its usage and get flag
+ *      EXHAUSTED.
+ * X and codes must be those of the fadkv_encode call of this step (codes is updated in
+ * place).  replaced: device [num_dicts][M] int32, the overwritten atom per row or -1.
+ * atoms and usage are updated in place; N never changes. */
+int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
+                const fadkv_codes *codes, int32_t *replaced, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* x_hat[t][m] = sum over non-empty slots k of coef[t][m][k] * atoms[t][idx[t][m][k]],
+ * written as out_dtype (fp32 accumulation; 16-bit outputs rounded to nearest even).
+ * idx entries must be -1 or in [0, N). */
+int fadkv_reconstruct(const fadkv_dict *dict, const int32_t *idx, const float *coef, int32_t s,
+                      int64_t M, void *X_hat, int32_t out_dtype, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *fadkv_status_string(int status);
+
+/* FADKV_ABI_VERSION of the built library. */
+int fadkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FADKV_H */

@@ -1,0 +1,278 @@
+// Fixed-size dictionary adaptation (FAD-KV Figure 2) and reconstruction.
+//
+// Commit of one step, per dictionary, after every vector was encoded against the dictionary as
+// it stood at step start:
+//   mark    (one thread per row)  : usage[j] += 1 for atoms of non-triggering codes (integer
+//                                   atomics: the result does not depend on their order) and
+//                                   mark every atom selected by any code of the step;
+//   select  (one block per dict)  : rank the triggering rows in row order; list the inactive
+//                                   atoms (usage < tau_c, unmarked) in (usage, index) order,
+//                                   one usage level at a time, until there is one per trigger;
+//   apply   (one wave per row)    : trigger k takes candidate k: the atom becomes x/||x||
+//                                   (fp64, rounded to the storage dtype), usage = 1, and the
+//                                   row is re-coded onto it with the one-atom ridge coefficient;
+//                                   triggers past the list keep their code and commit its usage.
+// No step depends on thread scheduling, so the outcome is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace fadkv {
+
+__global__ void adapt_clear_kernel(uint32_t *__restrict__ words, size_t count) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (size_t)gridDim.x * blockDim.x)
+    words[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void adapt_mark_kernel(const int32_t *__restrict__ idx,
+                                                         const uint8_t *__restrict__ flags,
+                                                         uint32_t *__restrict__ usage,
+                                                         uint8_t *__restrict__ touched,
+                                                         int touched_stride, int N, int M, int s,
+                                                         size_t G) {
+  const size_t gv = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gv >= G) return;
+  const int dict = (int)(gv / (size_t)M);
+  const uint8_t fl = flags[gv];
+  if (fl & FLAG_NONFINITE) return;
+  const bool commit = !(fl & FLAG_TRIGGER);
+  for (int k = 0; k < s; ++k) {
+    const int j = idx[gv * s + k];
+    if (j < 0 || j >= N) continue;
+    touched[(size_t)dict * touched_stride + j] = 1;
+    if (commit) atomicAdd(&usage[(size_t)dict * N + j], 1u);
+  }
+}
+
+namespace {
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+
+// exclusive prefix count of `pred` over the block in thread order; returns the total
+__device__ __forceinline__ int block_prefix(bool pred, int *s_w, int &prefix) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long mask = __ballot(pred);
+  const int below = __popcll(mask & ((1ull << lane) - 1ull));
+  if (lane == 0) s_w[wave] = __popcll(mask);
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int q = 0; q < SEL_WAVES; ++q) {
+    const int c = s_w[q];
+    before += q < wave ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  prefix = before + below;
+  return total;
+}
+
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t *s_w) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t w = __shfl_xor(v, o, 64);
+    v = w < v ? w : v;
+  }
+  if (lane == 0) s_w[wave] = v;
+  __syncthreads();
+  uint32_t m = s_w[0];
+  for (int q = 1; q < SEL_WAVES; ++q) m = s_w[q] < m ? s_w[q] : m;
+  __syncthreads();
+  return m;
+}
+}  // namespace
+
+__global__ __launch_bounds__(SEL_THREADS) void adapt_select_kernel(
+    const uint32_t *__restrict__ usage, const uint8_t *__restrict__ touched, int touched_stride,
+    const uint8_t *__restrict__ flags, int N, int M, uint32_t tau_c, int32_t *__restrict__ rank,
+    int32_t *__restrict__ cand, int32_t *__restrict__ ccount) {
+  __shared__ int s_w[SEL_WAVES];
+  __shared__ uint32_t s_u[SEL_WAVES];
+  const int dict = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t row0 = (size_t)dict * M;
+
+  int T = 0;
+  for (int m0 = 0; m0 < M; m0 += SEL_THREADS) {
+    const int m = m0 + tid;
+    const bool t = m < M && (flags[row0 + m] & FLAG_TRIGGER);
+    int prefix;
+    const int total = block_prefix(t, s_w, prefix);
+    if (m < M) rank[row0 + m] = t ? T + prefix : -1;
+    T += total;
+  }
+
+  const uint32_t *u = usage + (size_t)dict * N;
+  const uint8_t *tch = touched + (size_t)dict * touched_stride;
+  int count = 0;
+  unsigned long long floor_u = 0;   // usage levels below this are exhausted
+  while (count < T && floor_u < tau_c) {
+    uint32_t mine = 0xffffffffu;
+    for (int j = tid; j < N; j += SEL_THREADS) {
+      const uint32_t uj = u[j];
+      if (uj < tau_c && uj >= floor_u && !tch[j]) mine = uj < mine ? uj : mine;
+    }
+    const uint32_t level = block_min_u32(mine, s_u);
+    if (level == 0xffffffffu) break;
+    for (int j0 = 0; j0 < N && count < T; j0 += SEL_THREADS) {
+      const int j = j0 + tid;
+      const bool c = j < N && u[j] == level && !tch[j];
+      int prefix;
+      const int total = block_prefix(c, s_w, prefix);
+      if (c && count + prefix < T) cand[row0 + count + prefix] = j;
+      count += total;
+    }
+    floor_u = (unsigned long long)level + 1ull;
+  }
+  if (tid == 0) ccount[dict] = count < T ? count : T;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void adapt_apply_kernel(
+    uint8_t *__restrict__ atoms, uint32_t *__restrict__ usage, const uint8_t *__restrict__ X, int N,
+    int M, int s, float ridge_abs, float ridge_rel, const int32_t *__restrict__ rank,
+    const int32_t *__restrict__ cand, const int32_t *__restrict__ ccount, int32_t *__restrict__ idx,
+    float *__restrict__ coef, float *__restrict__ relerr, uint8_t *__restrict__ flags,
+    int32_t *__restrict__ replaced, size_t G) {
+  constexpr int ROWB = D * Elem<DT>::bytes;
+  constexpr int PER = D / 64;   // elements per lane
+  const int lane = threadIdx.x & 63;
+  const size_t gv = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gv >= G) return;
+  const int dict = (int)(gv / (size_t)M);
+  const int r = rank[gv];
+  if (r < 0) {
+    if (lane == 0) replaced[gv] = -1;
+    return;
+  }
+  if (r < ccount[dict]) {
+    const int j = cand[(size_t)dict * M + r];
+    const uint8_t *xr = X + gv * ROWB;
+    double x[PER];
+    double ss = 0.0;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      x[p] = (double)elem_f<DT>(xr, lane + 64 * p);
+      ss += x[p] * x[p];
+    }
+    const double nrm = __builtin_sqrt(wave_sum_d(ss));
+    uint8_t *arow = atoms + ((size_t)dict * N + j) * ROWB;
+    double a[PER];
+    double g = 0.0, ax = 0.0;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = lane + 64 * p;
+      const uint32_t bits = double_to_storage_bits<DT>(x[p] / nrm);
+      if constexpr (DT == DT_F32) {
+        reinterpret_cast<uint32_t *>(arow)[i] = bits;
+        a[p] = (double)__uint_as_float(bits);
+      } else {
+        reinterpret_cast<uint16_t *>(arow)[i] = (uint16_t)bits;
+        a[p] = (double)(DT == DT_F16 ? f16_bits_to_float(bits) : bf16_bits_to_float(bits));
+      }
+      g += a[p] * a[p];
+      ax += a[p] * x[p];
+    }
+    g = wave_sum_d(g);
+    ax = wave_sum_d(ax);
+    const double c = ax / ((1.0 + (double)ridge_rel) * g + (double)ridge_abs);
+    double rr = 0.0;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const double d = x[p] - c * a[p];
+      rr += d * d;
+    }
+    rr = wave_sum_d(rr);
+    if (lane < s) {
+      idx[gv * s + lane] = lane == 0 ? j : -1;
+      coef[gv * s + lane] = lane == 0 ? (float)c : 0.f;
+    }
+    if (lane == 0) {
+      usage[(size_t)dict * N + j] = 1u;
+      relerr[gv] = (float)(__builtin_sqrt(rr) / nrm);
+      flags[gv] = flags[gv] | FLAG_REPLACED;
+      replaced[gv] = j;
+    }
+  } else {
+    if (lane < s) {
+      const int jj = idx[gv * s + lane];
+      if (jj >= 0 && jj < N) atomicAdd(&usage[(size_t)dict * N + jj], 1u);
+    }
+    if (lane == 0) {
+      flags[gv] = flags[gv] | FLAG_EXHAUSTED;
+      replaced[gv] = -1;
+    }
+  }
+}
+
+template <int DT, int D, int ODT>
+__global__ __launch_bounds__(256) void reconstruct_kernel(const uint8_t *__restrict__ atoms,
+                                                          const int32_t *__restrict__ idx,
+                                                          const float *__restrict__ coef, int N,
+                                                          int M, int s, uint8_t *__restrict__ out,
+                                                          size_t G) {
+  constexpr int ROWB = D * Elem<DT>::bytes;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t gv = e / D;
+  const int i = (int)(e % D);
+  if (gv >= G) return;
+  const int dict = (int)(gv / (size_t)M);
+  float acc = 0.f;
+  for (int k = 0; k < s; ++k) {
+    const int j = idx[gv * s + k];
+    if (j < 0 || j >= N) continue;
+    acc = fmaf(coef[gv * s + k], elem_f<DT>(atoms + ((size_t)dict * N + j) * ROWB, i), acc);
+  }
+  if constexpr (ODT == DT_F32) reinterpret_cast<float *>(out)[e] = acc;
+  else if constexpr (ODT == DT_F16) reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)float_to_f16_bits(acc);
+  else reinterpret_cast<uint16_t *>(out)[e] = (uint16_t)float_to_bf16_bits(acc);
+}
+
+hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const void *X, int num_dicts,
+                        int N, int M, int s, float ridge_abs, float ridge_rel, uint32_t tau_c,
+                        int32_t *idx, float *coef, float *relerr, uint8_t *flags,
+                        int32_t *replaced, uint8_t *touched, int touched_stride, int32_t *rank,
+                        int32_t *cand, int32_t *ccount, hipStream_t stream) {
+  const size_t G = (size_t)num_dicts * M;
+  const size_t words = (size_t)num_dicts * touched_stride / 4;
+  hipLaunchKernelGGL(adapt_clear_kernel, dim3((unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096)),
+                     dim3(256), 0, stream, reinterpret_cast<uint32_t *>(touched), words);
+  hipLaunchKernelGGL(adapt_mark_kernel, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, stream, idx,
+                     flags, usage, touched, touched_stride, N, M, s, G);
+  hipLaunchKernelGGL(adapt_select_kernel, dim3(num_dicts), dim3(SEL_THREADS), 0, stream, usage,
+                     touched, touched_stride, flags, N, M, tau_c, rank, cand, ccount);
+  uint8_t *A = static_cast<uint8_t *>(atoms);
+  const uint8_t *Xb = static_cast<const uint8_t *>(X);
+  dim3 grid((unsigned)((G + 3) / 4)), block(256);
+#define L(DT, D)                                                                                   \
+  hipLaunchKernelGGL((adapt_apply_kernel<DT, D>), grid, block, 0, stream, A, usage, Xb, N, M, s,  \
+                     ridge_abs, ridge_rel, rank, cand, ccount, idx, coef, relerr, flags, replaced, G)
+  if (dtype == DT_F32) { if (d == 64) L(DT_F32, 64); else L(DT_F32, 128); }
+  else if (dtype == DT_F16) { if (d == 64) L(DT_F16, 64); else L(DT_F16, 128); }
+  else { if (d == 64) L(DT_BF16, 64); else L(DT_BF16, 128); }
+#undef L
+  return hipGetLastError();
+}
+
+hipError_t launch_reconstruct(int dtype, int d, const void *atoms, const int32_t *idx,
+                              const float *coef, int num_dicts, int N, int M, int s, void *out,
+                              int out_dtype, hipStream_t stream) {
+  const size_t G = (size_t)num_dicts * M;
+  const size_t E = G * d;
+  dim3 grid((unsigned)((E + 255) / 256)), block(256);
+  const uint8_t *A = static_cast<const uint8_t *>(atoms);
+  uint8_t *O = static_cast<uint8_t *>(out);
+#define L(DT, D, ODT) \
+  hipLaunchKernelGGL((reconstruct_kernel<DT, D, ODT>), grid, block, 0, stream, A, idx, coef, N, M, s, O, G)
+#define LO(DT, D) do { if (out_dtype == DT_F32) L(DT, D, DT_F32); else if (out_dtype == DT_F16) L(DT, D, DT_F16); else L(DT, D, DT_BF16); } while (0)
+#define LD(DT) do { if (d == 64) LO(DT, 64); else LO(DT, 128); } while (0)
+  if (dtype == DT_F32) LD(DT_F32);
+  else if (dtype == DT_F16) LD(DT_F16);
+  else LD(DT_BF16);
+#undef LD
+#undef LO
+#undef L
+  return hipGetLastError();
+}
+
+}  // namespace fadkv

@@ -1,0 +1,193 @@
+// C ABI of libfadkv (declared in include/fadkv.h): argument checks on the host, workspace
+// carving and kernel dispatch.  Nothing here allocates, synchronises or touches the GPU before
+// every argument has been accepted.
+#include "fadkv.h"
+
+#include <math.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxN = 65535;    // pool indices are stored as uint16
+constexpr int kMaxPool = 512;   // one selection thread per pool entry
+constexpr int kMaxS = 32;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int dtype_bytes(int dt) { return dt == FADKV_F32 ? 4 : 2; }
+
+struct Layout {
+  // encode
+  size_t pool_idx, pool_sig, vstat, encode_end;
+  // adapt
+  size_t touched, rank, cand, ccount, adapt_end;
+  int touched_stride;
+  size_t total;
+};
+
+Layout layout(const fadkv_dict *dict, const fadkv_params *p, int64_t M) {
+  Layout L{};
+  const size_t G = (size_t)dict->num_dicts * (size_t)M;
+  size_t o = 0;
+  L.pool_idx = o; o = align_up(o + G * (size_t)p->n * sizeof(uint16_t));
+  L.pool_sig = o; o = align_up(o + G * (size_t)p->n * sizeof(float));
+  L.vstat = o;    o = align_up(o + G);
+  L.encode_end = o;
+  o = 0;
+  L.touched_stride = (int)align_up((size_t)dict->N);
+  L.touched = o; o = align_up(o + (size_t)dict->num_dicts * L.touched_stride);
+  L.rank = o;    o = align_up(o + G * sizeof(int32_t));
+  L.cand = o;    o = align_up(o + G * sizeof(int32_t));
+  L.ccount = o;  o = align_up(o + (size_t)dict->num_dicts * sizeof(int32_t));
+  L.adapt_end = o;
+  L.total = L.encode_end > L.adapt_end ? L.encode_end : L.adapt_end;
+  return L;
+}
+
+int check_dict(const fadkv_dict *dict) {
+  if (!dict) return FADKV_ERR_ARG;
+  if (dict->dtype != FADKV_F32 && dict->dtype != FADKV_F16 && dict->dtype != FADKV_BF16)
+    return FADKV_ERR_DTYPE;
+  if (dict->num_dicts < 1 || dict->N < 1 || dict->N > kMaxN) return FADKV_ERR_SHAPE;
+  if (dict->d != 64 && dict->d != 128) return FADKV_ERR_SHAPE;
+  if (!dict->atoms || !aligned(dict->atoms, 16)) return FADKV_ERR_ARG;
+  return FADKV_OK;
+}
+
+int check_params(const fadkv_dict *dict, const fadkv_params *p) {
+  if (!p) return FADKV_ERR_ARG;
+  if (p->s < 1 || p->s > kMaxS || p->n < p->s || p->n > kMaxPool || p->n > dict->N)
+    return FADKV_ERR_SHAPE;
+  if (p->select != FADKV_SELECT_GM && p->select != FADKV_SELECT_PL) return FADKV_ERR_ARG;
+  if (!(p->ridge_abs >= 0.f) || !(p->ridge_rel >= 0.f) || !isfinite(p->ridge_abs) ||
+      !isfinite(p->ridge_rel))
+    return FADKV_ERR_ARG;
+  if (!(p->delta_key >= 0.f) || !(p->delta_value >= 0.f)) return FADKV_ERR_ARG;
+  return FADKV_OK;
+}
+
+int check_M(const fadkv_dict *dict, int64_t M) {
+  if (M < 0) return FADKV_ERR_ARG;
+  if ((double)dict->num_dicts * (double)M >= 2147483648.0) return FADKV_ERR_SHAPE;
+  return FADKV_OK;
+}
+
+int check_codes(const fadkv_codes *c) {
+  if (!c || !c->idx || !c->coef || !c->relerr || !c->flags) return FADKV_ERR_ARG;
+  if (!aligned(c->idx, 4) || !aligned(c->coef, 4) || !aligned(c->relerr, 4)) return FADKV_ERR_ARG;
+  return FADKV_OK;
+}
+
+#define FADKV_TRY(expr)        \
+  do {                         \
+    const int _st = (expr);    \
+    if (_st != FADKV_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int fadkv_abi_version(void) { return FADKV_ABI_VERSION; }
+
+const char *fadkv_status_string(int status) {
+  switch (status) {
+    case FADKV_OK: return "ok";
+    case FADKV_ERR_ARG: return "invalid argument (null or misaligned pointer, negative count or bad parameter)";
+    case FADKV_ERR_DTYPE: return "unsupported dtype";
+    case FADKV_ERR_SHAPE: return "shape outside the supported limits";
+    case FADKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case FADKV_ERR_HIP: return "HIP runtime or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int fadkv_workspace_bytes(const fadkv_dict *dict, const fadkv_params *params, int64_t M,
+                          size_t *bytes) {
+  if (!bytes) return FADKV_ERR_ARG;
+  if (!dict) return FADKV_ERR_ARG;
+  if (dict->dtype != FADKV_F32 && dict->dtype != FADKV_F16 && dict->dtype != FADKV_BF16)
+    return FADKV_ERR_DTYPE;
+  if (dict->num_dicts < 1 || dict->N < 1 || dict->N > kMaxN || (dict->d != 64 && dict->d != 128))
+    return FADKV_ERR_SHAPE;
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  *bytes = layout(dict, params, M).total;
+  return FADKV_OK;
+}
+
+int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
+                 const fadkv_codes *out, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  FADKV_TRY(check_codes(out));
+  if (M > 0 && (!X || !aligned(X, 16))) return FADKV_ERR_ARG;
+  const Layout L = layout(dict, params, M);
+  if (M > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total))
+    return FADKV_ERR_WORKSPACE;
+  if (M == 0) return FADKV_OK;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  uint16_t *pool_idx = reinterpret_cast<uint16_t *>(ws + L.pool_idx);
+  float *pool_sig = reinterpret_cast<float *>(ws + L.pool_sig);
+  uint8_t *vstat = ws + L.vstat;
+  if (fadkv::launch_score_topn(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N,
+                               (int)M, params->n, pool_idx, pool_sig, vstat, stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  if (fadkv::launch_select(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N, (int)M,
+                           params->n, params->s, params->select, params->ridge_abs,
+                           params->ridge_rel, params->delta_key, params->delta_value, pool_idx,
+                           pool_sig, vstat, out->idx, out->coef, out->relerr, out->flags,
+                           stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
+                const fadkv_codes *codes, int32_t *replaced, void *workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  FADKV_TRY(check_codes(codes));
+  if (!dict->usage || !aligned(dict->usage, 4)) return FADKV_ERR_ARG;
+  if (!replaced || !aligned(replaced, 4)) return FADKV_ERR_ARG;
+  if (M > 0 && (!X || !aligned(X, 16))) return FADKV_ERR_ARG;
+  const Layout L = layout(dict, params, M);
+  if (M > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total))
+    return FADKV_ERR_WORKSPACE;
+  if (M == 0) return FADKV_OK;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  if (fadkv::launch_adapt(dict->dtype, dict->d, dict->atoms, dict->usage, X, dict->num_dicts,
+                          dict->N, (int)M, params->s, params->ridge_abs, params->ridge_rel,
+                          params->tau_c, codes->idx, codes->coef, codes->relerr, codes->flags,
+                          replaced, ws + L.touched, L.touched_stride,
+                          reinterpret_cast<int32_t *>(ws + L.rank),
+                          reinterpret_cast<int32_t *>(ws + L.cand),
+                          reinterpret_cast<int32_t *>(ws + L.ccount), stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_reconstruct(const fadkv_dict *dict, const int32_t *idx, const float *coef, int32_t s,
+                      int64_t M, void *X_hat, int32_t out_dtype, hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_M(dict, M));
+  if (s < 1 || s > kMaxS) return FADKV_ERR_SHAPE;
+  if (out_dtype != FADKV_F32 && out_dtype != FADKV_F16 && out_dtype != FADKV_BF16)
+    return FADKV_ERR_DTYPE;
+  if (M == 0) return FADKV_OK;
+  if (!idx || !coef || !X_hat || !aligned(idx, 4) || !aligned(coef, 4) || !aligned(X_hat, 16))
+    return FADKV_ERR_ARG;
+  if (fadkv::launch_reconstruct(dict->dtype, dict->d, dict->atoms, idx, coef, dict->num_dicts,
+                                dict->N, (int)M, s, X_hat, out_dtype, stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Host-side launchers of the FAD-KV kernels (internal to libfadkv; see include/fadkv.h for the
+// public C ABI).  Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fadkv {
+
+hipError_t launch_score_topn(int dtype, int d, const void *atoms, const void *X, int num_dicts,
+                             int N, int M, int n, uint16_t *pool_idx, float *pool_sig,
+                             uint8_t *vstat, hipStream_t stream);
+
+hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int num_dicts, int N,
+                         int M, int n, int s, int select, float ridge_abs, float ridge_rel,
+                         float delta_key, float delta_value, const uint16_t *pool_idx,
+                         const float *pool_sig, const uint8_t *vstat, int32_t *idx, float *coef,
+                         float *relerr, uint8_t *flags, hipStream_t stream);
+
+hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const void *X, int num_dicts,
+                        int N, int M, int s, float ridge_abs, float ridge_rel, uint32_t tau_c,
+                        int32_t *idx, float *coef, float *relerr, uint8_t *flags,
+                        int32_t *replaced, uint8_t *touched, int touched_stride, int32_t *rank,
+                        int32_t *cand, int32_t *ccount, hipStream_t stream);
+
+hipError_t launch_reconstruct(int dtype, int d, const void *atoms, const int32_t *idx,
+                              const float *coef, int num_dicts, int N, int M, int s, void *out,
+                              int out_dtype, hipStream_t stream);
+
+}  // namespace fadkv

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/fadkv.h
+declares, sizes workspaces, and rejects bad arguments on the host before enqueuing anything.
+
+Invalid calls use fake (never dereferenced) device addresses: argument checking returns before
+any HIP call, so no GPU is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_dictionary_coding_amd import fadkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fadkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fadkv.LIB_PATH),
+                                reason="libfadkv.so not built (run __graft_entry__.build())")
+
+FAKE = 0x7F0000100000          # 256-byte aligned, never dereferenced by the host checks
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fadkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for fn in ("fadkv_encode", "fadkv_adapt", "fadkv_reconstruct", "fadkv_workspace_bytes",
+               "fadkv_status_string", "fadkv_abi_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_function():
+    h = ctypes.CDLL(fadkv.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(h, fn), f"{fn} declared in fadkv.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert fadkv.fadkv_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert fadkv.fadkv_status_string(st) and fadkv.fadkv_status_string(st) != "unknown status"
+    assert fadkv.fadkv_status_string(-99) == "unknown status"
+
+
+def _dict(num_dicts=2, N=1024, d=128, dtype=fadkv.FADKV_F16, atoms=FAKE, usage=FAKE):
+    return fadkv.fadkv_dict(num_dicts, N, d, dtype, atoms, usage)
+
+
+def _params(**kw):
+    base = dict(n=256, s=8, ridge_abs=1e-4, ridge_rel=0.2, delta_key=0.5, delta_value=0.7,
+                tau_c=1, select=0)
+    base.update(kw)
+    return fadkv.fadkv_params(**base)
+
+
+def _ws(dd, pp, M):
+    out = ctypes.c_size_t(0)
+    st = fadkv.lib().fadkv_workspace_bytes(ctypes.byref(dd), ctypes.byref(pp), M, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_bytes_covers_pool_and_adapt_buffers():
+    st, b = _ws(_dict(num_dicts=56, N=4096), _params(), 256)
+    assert st == 0
+    G = 56 * 256
+    assert b >= G * 256 * 6 + G           # pool indices (u16) + pool scores (f32) + status
+    st, b2 = _ws(_dict(num_dicts=56, N=4096), _params(), 512)
+    assert st == 0 and b2 > b
+    st, b0 = _ws(_dict(), _params(), 0)
+    assert st == 0
+
+
+@pytest.mark.parametrize("bad,expect", [
+    (dict(d=96), -3), (dict(d=0), -3), (dict(N=0), -3), (dict(N=70000), -3),
+    (dict(num_dicts=0), -3), (dict(dtype=7), -2),
+])
+def test_workspace_rejects_bad_dictionaries(bad, expect):
+    st, _ = _ws(_dict(**bad), _params(), 10)
+    assert st == expect
+
+
+@pytest.mark.parametrize("bad,expect", [
+    (dict(s=0), -3), (dict(s=33, n=64), -3), (dict(n=4, s=8), -3), (dict(n=513), -3),
+    (dict(n=2048), -3), (dict(select=5), -1), (dict(ridge_abs=-1.0), -1),
+    (dict(ridge_rel=float("nan")), -1), (dict(delta_key=float("nan")), -1),
+    (dict(delta_value=-0.1), -1),
+])
+def test_workspace_rejects_bad_params(bad, expect):
+    st, _ = _ws(_dict(), _params(**bad), 10)
+    assert st == expect
+
+
+def _codes(ptr=FAKE):
+    return fadkv.fadkv_codes(ptr, ptr, ptr, ptr)
+
+
+def _encode(dd, pp, X=FAKE, M=10, codes=None, ws=FAKE, ws_bytes=1 << 40):
+    return fadkv.lib().fadkv_encode(ctypes.byref(dd), ctypes.byref(pp), X, M,
+                                    ctypes.byref(codes or _codes()), ws, ws_bytes, None)
+
+
+def test_encode_argument_checks_return_before_any_launch():
+    assert _encode(_dict(atoms=None), _params()) == -1
+    assert _encode(_dict(atoms=FAKE + 8), _params()) == -1        # atoms not 16-byte aligned
+    assert _encode(_dict(), _params(), X=None) == -1
+    assert _encode(_dict(), _params(), X=FAKE + 4) == -1
+    assert _encode(_dict(), _params(), M=-1) == -1
+    assert _encode(_dict(), _params(), codes=fadkv.fadkv_codes(FAKE, None, FAKE, FAKE)) == -1
+    assert _encode(_dict(), _params(), codes=fadkv.fadkv_codes(FAKE + 2, FAKE, FAKE, FAKE)) == -1
+    assert _encode(_dict(), _params(), ws=None) == -4
+    assert _encode(_dict(), _params(), ws_bytes=100) == -4
+    assert _encode(_dict(num_dicts=1 << 20), _params(), M=1 << 12) == -3   # >= 2^31 vectors
+    assert _encode(_dict(dtype=3), _params()) == -2
+    assert _encode(_dict(), _params(n=2000)) == -3
+
+
+def test_encode_with_no_vectors_is_a_no_op():
+    # M = 0: everything checked, nothing launched, no workspace needed
+    assert _encode(_dict(), _params(), X=None, M=0, ws=None, ws_bytes=0) == 0
+
+
+def test_adapt_argument_checks():
+    L = fadkv.lib()
+
+    def adapt(dd, pp, X=FAKE, M=10, replaced=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return L.fadkv_adapt(ctypes.byref(dd), ctypes.byref(pp), X, M, ctypes.byref(_codes()),
+                             replaced, ws, ws_bytes, None)
+
+    assert adapt(_dict(usage=None), _params()) == -1
+    assert adapt(_dict(usage=FAKE + 2), _params()) == -1
+    assert adapt(_dict(), _params(), replaced=None) == -1
+    assert adapt(_dict(), _params(), ws_bytes=10) == -4
+    assert adapt(_dict(), _params(), M=0, X=None, ws=None, ws_bytes=0) == 0
+
+
+def test_reconstruct_argument_checks():
+    L = fadkv.lib()
+
+    def rec(dd, idx=FAKE, coef=FAKE, s=8, M=10, out=FAKE, odt=1):
+        return L.fadkv_reconstruct(ctypes.byref(dd), idx, coef, s, M, out, odt, None)
+
+    assert rec(_dict(), idx=None) == -1
+    assert rec(_dict(), out=FAKE + 8) == -1
+    assert rec(_dict(), s=0) == -3
+    assert rec(_dict(), s=40) == -3
+    assert rec(_dict(), odt=9) == -2
+    assert rec(_dict(), M=0) == 0
