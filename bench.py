@@ -1,0 +1,201 @@
+"""Benchmark of the FAD-KV encoder hot path on one MI355X.
+
+One step = one batch of key/value head vectors through every stage: screening + Top-n pool
+(fadkv_screen), support/ridge/residual (fadkv_select_support) and the fixed-size adaptation
+commit (fadkv_adapt).  Inputs are synthetic and already resident in HBM when timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3b_decode]
+
+Prints one JSON line (rank 0).  `value` is encoded vectors per second over the K timed steps
+(wall clock, synchronised on both sides).  Each stage is also bracketed by HIP events on the
+stream the library launches on; the dominant kernel's average duration gives `roofline`.
+By default the step rotates over enough independent dictionary sets to exceed the 256 MB
+Infinity Cache, so the dictionaries stream from HBM (`--warm` keeps one set).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "encoded KV vectors/sec (decode step & prefill) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16/fp16 (256 CU x 2.4 GHz x 4096 flop/clk)
+ALU_PEAK_TFLOPS = 157.3          # 256 CU x 64 lanes x 2.4 GHz x 4 flop (v_dot2_f32_{f16,bf16})
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3b_decode")
+    ap.add_argument("--select", default="gm", choices=["gm", "pl"])
+    ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, select, seconds):
+    """Time the CPU oracle, as it stands, on whole dictionaries of the same workload until
+    about `seconds` of work: encode every row of a dictionary, then commit its adaptation."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_dictionary_coding_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    p = oracle.OracleParams(n=w.n, s=w.s, select=select,
+                            ridge_abs=float(np.float32(1e-4)), ridge_rel=float(np.float32(0.2)))
+    gen = synth.SyntheticKV(w, device="cpu", num_dicts=min(w.num_dicts, 64))
+    A = synth.to_f64(gen.atoms())
+    rows_per_dict = min(w.M, 256)
+    X = synth.to_f64(gen.batch(torch.from_numpy(A).to(synth.TORCH_DTYPES[w.dtype]),
+                               M=rows_per_dict))
+    done = 0
+    dicts = 0
+    t0 = time.perf_counter()
+    for t in range(gen.T):
+        codes = oracle.encode(A[t:t + 1], X[t:t + 1], p, dict_ids=[t])
+        oracle.adapt(A[t:t + 1], np.zeros((1, w.N), np.int64), X[t:t + 1], codes, p, w.dtype)
+        done += rows_per_dict
+        dicts += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "vectors/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{dicts} of {w.num_dicts} dictionaries x {rows_per_dict} vectors "
+                      f"(encode + adapt, NumPy fp64), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(dictionaries shard by layer with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_dictionary_coding_amd import fadkv, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    p = fadkv.Params(n=w.n, s=w.s, select=args.select)
+    T, M, N, d = w.num_dicts, w.M, w.N, w.d
+    esize = 2 if w.dtype != "f32" else 4
+    dict_bytes = T * N * d * esize
+    R = 1 if args.warm else max(1, -(-(MALL_BYTES + (MALL_BYTES >> 2)) // dict_bytes))
+    R = min(R, 8)
+
+    gen = synth.SyntheticKV(w, device=dev)
+    base_atoms = gen.atoms()
+    sets = [base_atoms.clone() for _ in range(R)]
+    usages = [torch.zeros(T, N, dtype=torch.int32, device=dev) for _ in range(R)]
+    n_batches = min(args.steps + args.warmup, 16 if M * T <= 65536 else 1)
+    batches = [gen.batch(base_atoms, step=i) for i in range(n_batches)]
+    pool = fadkv.Pool.empty(T, M, w.n, dev)
+    codes = fadkv.Codes.empty(T, M, w.s, dev)
+    replaced = torch.empty(T, M, dtype=torch.int32, device=dev)
+    ws = fadkv.make_workspace(base_atoms, p, M)
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        A, U, X = sets[k % R], usages[k % R], batches[k % n_batches]
+        if ev is not None:
+            ev[0].record(stream)
+        fadkv.fadkv_screen(A, X, p, out=pool, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fadkv.fadkv_select_support(A, X, p, pool, out=codes, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fadkv.fadkv_adapt(A, U, X, codes, p, replaced=replaced, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = [0.0, 0.0, 0.0]
+    for e in evs:
+        for i in range(3):
+            stage_ms[i] += e[i].elapsed_time(e[i + 1])
+    stage_ms = [x / args.steps for x in stage_ms]
+    G = T * M
+    vec_per_step = G
+    value = vec_per_step * args.steps / wall
+
+    # algorithmic work per launch
+    screen_flops = 2.0 * N * d * G
+    screen_bytes = dict_bytes + G * d * esize + G * w.n * 6 + G
+    sel_cols = (w.s - 1) if args.select == "gm" else 0
+    sel_flops = 2.0 * G * (sel_cols * w.n * d + w.s * w.s * d / 2 + w.s * d)
+    adapt_bytes = G * (w.s * 8 + 5) + 2 * T * N * 4
+    kernels = {
+        "screen_topn": {"ms": stage_ms[0], "flops": screen_flops, "bytes": screen_bytes},
+        "select_support": {"ms": stage_ms[1], "flops": sel_flops},
+        "adapt": {"ms": stage_ms[2], "bytes": adapt_bytes},
+    }
+    dominant = max(("screen_topn", "select_support"), key=lambda k: kernels[k]["ms"])
+    if dominant == "screen_topn":
+        ach = screen_flops / (stage_ms[0] * 1e-3) / 1e12
+        roof = {"kernel": "score_topn_kernel", "bound": "mfma", "achieved": ach,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": None}
+    else:
+        ach = sel_flops / (stage_ms[1] * 1e-3) / 1e12
+        roof = {"kernel": "select_kernel", "bound": "alu", "achieved": ach,
+                "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / ALU_PEAK_TFLOPS,
+                "traffic": None}
+    # the screening kernel against HBM as well (the decode-step figure of merit)
+    screen_gbs = screen_bytes / (stage_ms[0] * 1e-3) / 1e9
+    trig = int((codes.flags & fadkv.FLAG_TRIGGER).ne(0).sum().item())
+    rep = int((replaced >= 0).sum().item())
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_dicts": T, "vectors_per_dict": M, "N": N, "n": w.n,
+                   "s": w.s, "d": d, "select": args.select,
+                   "dictionary_sets": R, "cache": "warm" if R == 1 else
+                   f"cold: {R} rotating dictionary sets ({R * dict_bytes / 2**20:.0f} MiB)"},
+        "roofline": roof,
+        "kernels": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "screen_hbm": {"achieved": screen_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": screen_gbs / HBM_PEAK_GBS},
+        "last_step": {"triggers": trig, "replaced": rep},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.select, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

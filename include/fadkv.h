@@ -120,6 +120,26 @@ int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void 
                  const fadkv_codes *out, void *workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/* The two stages of fadkv_encode, for callers that want the candidate pool itself (e.g. to
+ * measure how much of a full pursuit's support it recalls, Figure 1b) or to time each stage.
+ *
+ * fadkv_screen -- abstract and Figure 1: scores sigma_j = <d_j, x> of every atom and the pool
+ * of the n largest |sigma| (ties to the lowest index).
+ *   pool_idx:   device uint16 [num_dicts][M][n], the pool's atom indices (unordered set);
+ *   pool_score: device float  [num_dicts][M][n], sigma of each pool atom (fp32 accumulation);
+ *   vstatus:    device uint8  [num_dicts][M], 0 = encoded, 1 = zero vector, 2 = non-finite
+ *               input (pool rows of status 1 and 2 are left unwritten).
+ * Needs no workspace. */
+int fadkv_screen(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
+                 uint16_t *pool_idx, float *pool_score, uint8_t *vstatus, hipStream_t stream);
+
+/* fadkv_select_support -- Tables 1-5: the s-atom support inside each pool (GM or PL), the
+ * ridge coefficients and the relative residual against delta, from fadkv_screen's outputs
+ * (same dict, params, X and M).  Writes `out` exactly as fadkv_encode does. */
+int fadkv_select_support(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                         int64_t M, const uint16_t *pool_idx, const float *pool_score,
+                         const uint8_t *vstatus, const fadkv_codes *out, hipStream_t stream);
+
 /* Commit one step's codes and apply fixed-size adaptation (Figure 2), per dictionary:
  *   1. usage[j] += 1 for every atom of every non-triggering code;
  *   2. candidates = atoms with usage < tau_c that no code of this step selected, ordered by

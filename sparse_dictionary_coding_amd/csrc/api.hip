@@ -18,8 +18,6 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int dtype_bytes(int dt) { return dt == FADKV_F32 ? 4 : 2; }
-
 struct Layout {
   // encode
   size_t pool_idx, pool_sig, vstat, encode_end;
@@ -143,6 +141,41 @@ int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void 
                            params->n, params->s, params->select, params->ridge_abs,
                            params->ridge_rel, params->delta_key, params->delta_value, pool_idx,
                            pool_sig, vstat, out->idx, out->coef, out->relerr, out->flags,
+                           stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_screen(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
+                 uint16_t *pool_idx, float *pool_score, uint8_t *vstatus, hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  if (M == 0) return FADKV_OK;
+  if (!X || !aligned(X, 16)) return FADKV_ERR_ARG;
+  if (!pool_idx || !pool_score || !vstatus || !aligned(pool_idx, 2) || !aligned(pool_score, 4))
+    return FADKV_ERR_ARG;
+  if (fadkv::launch_score_topn(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N,
+                               (int)M, params->n, pool_idx, pool_score, vstatus, stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_select_support(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                         int64_t M, const uint16_t *pool_idx, const float *pool_score,
+                         const uint8_t *vstatus, const fadkv_codes *out, hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  FADKV_TRY(check_codes(out));
+  if (M == 0) return FADKV_OK;
+  if (!X || !aligned(X, 16)) return FADKV_ERR_ARG;
+  if (!pool_idx || !pool_score || !vstatus || !aligned(pool_idx, 2) || !aligned(pool_score, 4))
+    return FADKV_ERR_ARG;
+  if (fadkv::launch_select(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N, (int)M,
+                           params->n, params->s, params->select, params->ridge_abs,
+                           params->ridge_rel, params->delta_key, params->delta_value, pool_idx,
+                           pool_score, vstatus, out->idx, out->coef, out->relerr, out->flags,
                            stream) != hipSuccess)
     return FADKV_ERR_HIP;
   return FADKV_OK;

@@ -71,6 +71,14 @@ def lib() -> ctypes.CDLL:
         h.fadkv_encode.restype = ctypes.c_int
         h.fadkv_encode.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p, ctypes.c_int64,
                                    P(fadkv_codes), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        h.fadkv_screen.restype = ctypes.c_int
+        h.fadkv_screen.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+        h.fadkv_select_support.restype = ctypes.c_int
+        h.fadkv_select_support.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, P(fadkv_codes), ctypes.c_void_p]
         h.fadkv_adapt.restype = ctypes.c_int
         h.fadkv_adapt.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p, ctypes.c_int64,
                                   P(fadkv_codes), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -193,6 +201,57 @@ def fadkv_encode(atoms: torch.Tensor, X: torch.Tensor, params: Params,
                             _stream(stream))
     if st != FADKV_OK:
         raise FadkvError("fadkv_encode", st)
+    return out
+
+
+@dataclass
+class Pool:
+    idx: torch.Tensor      # int16 storage of uint16 atom indices [num_dicts][M][n]
+    score: torch.Tensor    # float32 [num_dicts][M][n]
+    status: torch.Tensor   # uint8 [num_dicts][M]: 0 encoded, 1 zero vector, 2 non-finite
+
+    @staticmethod
+    def empty(num_dicts: int, M: int, n: int, device) -> "Pool":
+        return Pool(torch.empty(num_dicts, M, n, dtype=torch.int16, device=device),
+                    torch.empty(num_dicts, M, n, dtype=torch.float32, device=device),
+                    torch.empty(num_dicts, M, dtype=torch.uint8, device=device))
+
+    def atom_indices(self) -> torch.Tensor:
+        """Pool indices as int64 (the uint16 values)."""
+        return self.idx.to(torch.int64) & 0xFFFF
+
+
+def fadkv_screen(atoms: torch.Tensor, X: torch.Tensor, params: Params,
+                 out: Optional[Pool] = None, stream=None) -> Pool:
+    """Scores and Top-n pool of every vector (first stage of fadkv_encode)."""
+    dd = _dict(atoms)
+    T, N, d = atoms.shape
+    _check(X, "X", atoms.dtype)
+    M = X.shape[1]
+    if out is None:
+        out = Pool.empty(T, M, params.n, atoms.device)
+    st = lib().fadkv_screen(ctypes.byref(dd), ctypes.byref(params.c()), X.data_ptr(), M,
+                            out.idx.data_ptr(), out.score.data_ptr(), out.status.data_ptr(),
+                            _stream(stream))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_screen", st)
+    return out
+
+
+def fadkv_select_support(atoms: torch.Tensor, X: torch.Tensor, params: Params, pool: Pool,
+                         out: Optional[Codes] = None, stream=None) -> Codes:
+    """Support, ridge coefficients and residual from a screened pool (second stage)."""
+    dd = _dict(atoms)
+    T, N, d = atoms.shape
+    _check(X, "X", atoms.dtype)
+    M = X.shape[1]
+    if out is None:
+        out = Codes.empty(T, M, params.s, atoms.device)
+    st = lib().fadkv_select_support(ctypes.byref(dd), ctypes.byref(params.c()), X.data_ptr(), M,
+                                    pool.idx.data_ptr(), pool.score.data_ptr(),
+                                    pool.status.data_ptr(), ctypes.byref(out.c()), _stream(stream))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_select_support", st)
     return out
 
 

@@ -54,7 +54,7 @@ def oracle_codes_to_gpu(oc: oracle.Codes, device) -> fadkv.Codes:
     return fadkv.Codes(torch.from_numpy(oc.idx.astype(np.int32)).to(device),
                        torch.from_numpy(oc.coef.astype(np.float32)).to(device),
                        torch.from_numpy(oc.relerr.astype(np.float32)).to(device),
-                       torch.from_numpy((oc.flags & ~FLAG_NEAR_TIE).astype(np.uint8)).to(device))
+                       torch.from_numpy((oc.flags & np.uint8(0xFF ^ FLAG_NEAR_TIE)).astype(np.uint8)).to(device))
 
 
 @dataclass
