@@ -120,4 +120,31 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// ---- wave64 reductions through DPP (row-internal patterns, then the four row leaders) ------
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror: afterwards every lane
+// of a 16-lane row holds the row's reduction
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(dpp_i<0xB1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<0x4E>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<0x141>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<0x140>(__float_as_int(v))));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
 }  // namespace fadkv

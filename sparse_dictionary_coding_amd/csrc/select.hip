@@ -15,15 +15,21 @@
 // which needs one pool-wide column G_{P,j*} = D_P d_j* per step (skipped after the last
 // step) and O(k) work per pool atom.  At the end c = L^{-T} y by back substitution.
 // PL takes the s largest |sigma| of the pool the same way (no rho update) and solves once.
-// Finally r = x - D_S^T c is formed from the stored atoms and e = ||r|| / ||x||.
+// Finally r = x - D_S^T c is formed from the chosen rows and e = ||r|| / ||x||.
+//
+// Each step costs two workgroup barriers: (1) after every wave has published its local
+// argmax (wave reduction through DPP), (2) after the winner has published its row, its W row
+// and its diagonal.  The LDS slots they use are double-buffered by step parity, so no third
+// barrier is needed before they are rewritten.
 #include "common.h"
 #include "kernels.h"
 
 namespace fadkv {
 
 namespace {
-typedef unsigned long long u64;
 constexpr int MAX_THREADS = 512;
+constexpr int MAX_WAVES = MAX_THREADS / 64;
+constexpr int STAGE_ROWS = 16;
 }  // namespace
 
 template <int DT, int D> struct RowWords {
@@ -68,25 +74,45 @@ __device__ __forceinline__ float row_self_dot(const uint32_t (&a)[NW]) {
   return s0 + s1;
 }
 
+// element i of a packed row held in LDS
+template <int DT> __device__ __forceinline__ float lds_elem(const uint32_t *row, int i) {
+  if constexpr (DT == DT_F32) return __uint_as_float(row[i]);
+  else return (i & 1) ? hi_f<DT>(row[i >> 1]) : lo_f<DT>(row[i >> 1]);
+}
+
 template <int DT, int D, int SMAX>
 __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
-    const uint8_t *__restrict__ atoms, const uint8_t *__restrict__ X, int N, int M, int n, int s,
-    int select, float ridge_abs, float ridge_rel, float delta_key, float delta_value,
+    const uint8_t *__restrict__ atoms, const uint8_t *__restrict__ X, int num_dicts, int N, int M,
+    int n, int s, int select, float ridge_abs, float ridge_rel, float delta_key, float delta_value,
     const uint16_t *__restrict__ pool_idx, const float *__restrict__ pool_sig,
     const uint8_t *__restrict__ vstat, int32_t *__restrict__ out_idx, float *__restrict__ out_coef,
     float *__restrict__ out_relerr, uint8_t *__restrict__ out_flags) {
   constexpr int NW = RowWords<DT, D>::NW;
   constexpr int ROWB = RowWords<DT, D>::ROWB;
-  __shared__ __attribute__((aligned(16))) uint32_t s_bc[NW];      // broadcast atom j*
-  __shared__ __attribute__((aligned(16))) uint32_t s_selrow[SMAX][NW];  // PL: chosen atoms
+  __shared__ __attribute__((aligned(16))) uint32_t s_bc[2][NW];        // winner's row, by parity
+  __shared__ __attribute__((aligned(16))) uint32_t s_selrow[SMAX][NW];  // chosen rows
   __shared__ float s_x[D];
   __shared__ float s_L[SMAX * SMAX];
-  __shared__ float s_y[SMAX], s_c[SMAX], s_l[SMAX], s_sig[SMAX], s_gdiag[SMAX];
+  __shared__ float s_y[SMAX], s_c[SMAX], s_sig[SMAX], s_gdiag[SMAX];
+  __shared__ float s_l[2][SMAX];
   __shared__ int s_sel[SMAX];
-  __shared__ u64 s_red[MAX_THREADS / 64];
-  __shared__ float s_sum[2][MAX_THREADS / 64];
+  __shared__ float s_rv[2][MAX_WAVES];
+  __shared__ int s_rj[2][MAX_WAVES];
+  __shared__ float s_sum[2][MAX_WAVES];
+  // per-wave staging of STAGE_ROWS rows, one 16-byte pad per row against bank conflicts
+  __shared__ __attribute__((aligned(16))) uint32_t s_stage[MAX_WAVES][STAGE_ROWS * (ROWB / 4 + 4)];
 
-  const size_t gv = blockIdx.x;
+  // With a multiple of 8 dictionaries, workgroup i (dispatched to XCD i % 8) takes a vector of
+  // dictionary xcd + 8 * (r / M), r = i / 8: each dictionary's pool rows are gathered through
+  // one XCD's L2.
+  size_t gv;
+  if ((num_dicts & 7) == 0) {
+    const size_t r = blockIdx.x / 8;
+    const int xcd = blockIdx.x % 8;
+    gv = (size_t)(xcd + 8 * (int)(r / (size_t)M)) * M + r % (size_t)M;
+  } else {
+    gv = blockIdx.x;
+  }
   const int dict = (int)(gv / (size_t)M);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -107,22 +133,50 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
 
   const uint8_t *dict_atoms = atoms + (size_t)dict * N * ROWB;
   const bool act = tid < n;
-  int j = 0;
+  int j = 0x7fffffff;
   float sig = 0.f;
-  uint32_t w[NW];
   if (act) {
-    j = pool_idx[gv * n + tid];
-    j = j < N ? j : N - 1;   // the screening kernel writes indices < N; never read past the set
+    const int jj = pool_idx[gv * n + tid];
+    j = jj < N ? jj : N - 1;   // the screening kernel writes indices < N; never read past the set
     sig = pool_sig[gv * n + tid];
-    const uint4 *src = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)j * ROWB);
+  }
+  // Gather the pool rows with whole-row coalesced loads: CPR lanes cover one row (16 bytes
+  // each), so a wave instruction reads 64/CPR complete rows; rows pass through a per-wave LDS
+  // stage of 16 rows and each thread then takes its own row from there.
+  uint32_t w[NW];
+  {
+    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;           // rows per wave instruction
+    uint4 *stage = reinterpret_cast<uint4 *>(s_stage[wave]);
+    const int base_row = wave * 64;
 #pragma unroll
-    for (int q = 0; q < NW / 4; ++q) {
-      const uint4 v = src[q];
-      w[4 * q + 0] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+    for (int g = 0; g < 64 / STAGE_ROWS; ++g) {
+#pragma unroll
+      for (int i = 0; i < STAGE_ROWS / RPI; ++i) {
+        const int r = g * STAGE_ROWS + i * RPI + lane / CPR;   // row within this wave's 64
+        const int t = base_row + r;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < n) {
+          int jr = pool_idx[gv * n + t];
+          jr = jr < N ? jr : N - 1;
+          v = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)jr * ROWB)[lane % CPR];
+        }
+        stage[(i * RPI + lane / CPR) * (CPR + 1) + lane % CPR] = v;
+      }
+      // same wave wrote the stage: LDS operations of one wave complete in order
+      if (lane / STAGE_ROWS == g) {
+        const int r = lane % STAGE_ROWS;
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q) {
+          const uint4 v = stage[r * (CPR + 1) + q];
+          w[4 * q + 0] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+        }
+      }
     }
-  } else {
+    if (!act) {
 #pragma unroll
-    for (int q = 0; q < NW; ++q) w[q] = 0u;
+      for (int q = 0; q < NW; ++q) w[q] = 0u;
+    }
   }
   for (int i = tid; i < D; i += blockDim.x) s_x[i] = elem_f<DT>(X + gv * ROWB, i);
   if (tid < SMAX) s_sel[tid] = 0;   // every slot names a valid row even if no thread wins
@@ -137,58 +191,71 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
 #pragma unroll
   for (int k = 0; k < SMAX; ++k) {
     if (k < s) {
-    // block argmax of |rho| (ties to the lowest atom index) over unchosen pool entries
-    const u64 key = (act && !chosen)
-                        ? (((u64)(__float_as_uint(rho) & 0x7fffffffu) << 32) | (u64)(0xFFFFFFFFu - (uint32_t)j))
-                        : 0ull;
-    const u64 wm = wave_max_u64(key);
-    if (lane == 0) s_red[wave] = wm;
-    __syncthreads();
-    u64 best = s_red[0];
-    for (int q = 1; q < nwaves; ++q) best = s_red[q] > best ? s_red[q] : best;
-    if (key == best && key != 0ull) {
-      chosen = true;
-#pragma unroll
-      for (int q = 0; q < NW; ++q) s_bc[q] = w[q];
-      if (!gm) {
-#pragma unroll
-        for (int q = 0; q < NW; ++q) s_selrow[k][q] = w[q];
+      const int buf = k & 1;
+      // (1) wave argmax of |rho| over unchosen entries, ties to the lowest atom index
+      const bool elig = act && !chosen;
+      const float v = elig ? fabsf(rho) : -1.f;
+      const float wmax = wave_max_f32(v);
+      const unsigned long long hit = __ballot(elig && v == wmax);
+      int wj;
+      if (__popcll(hit) == 1) wj = __builtin_amdgcn_readlane(j, (int)__ffsll((long long)hit) - 1);
+      else wj = wave_min_i32((elig && v == wmax) ? j : 0x7fffffff);
+      if (lane == 0) {
+        s_rv[buf][wave] = wmax;
+        s_rj[buf][wave] = wj;
       }
-      s_sel[k] = j;
-      s_sig[k] = sig;
-#pragma unroll
-      for (int m = 0; m < k; ++m) s_l[m] = W[m];
-      s_gdiag[k] = row_self_dot<DT, NW>(w);
-    }
-    __syncthreads();
-    if (gm) {
-      float nl2 = 0.f, ly = 0.f;
-#pragma unroll
-      for (int m = 0; m < k; ++m) {
-        const float l = s_l[m];
-        nl2 = fmaf(l, l, nl2);
-        ly = fmaf(l, s_y[m], ly);
-      }
-      const float alpha = fmaf(s_gdiag[k], 1.f + ridge_rel, ridge_abs);
-      const float Lkk = sqrtf(fmaxf(alpha - nl2, 1e-30f));
-      const float yk = (s_sig[k] - ly) / Lkk;
-      if (k + 1 < s) {
-        float acc = row_dot<DT, NW>(w, s_bc);
-#pragma unroll
-        for (int m = 0; m < k; ++m) acc = fmaf(-W[m], s_l[m], acc);
-        W[k] = acc / Lkk;
-        rho = fmaf(-W[k], yk, rho);
-      }
-      __syncthreads();   // everyone has read s_l / s_y / s_bc of this step
-      if (tid == 0) {
-#pragma unroll
-        for (int m = 0; m < k; ++m) s_L[k * SMAX + m] = s_l[m];
-        s_L[k * SMAX + k] = Lkk;
-        s_y[k] = yk;
-      }
-    } else {
       __syncthreads();
-    }
+      float bv = s_rv[buf][0];
+      int bj = s_rj[buf][0];
+      for (int q = 1; q < nwaves; ++q) {
+        const float qv = s_rv[buf][q];
+        const int qj = s_rj[buf][q];
+        if (qv > bv || (qv == bv && qj < bj)) {
+          bv = qv;
+          bj = qj;
+        }
+      }
+      // (2) the winner publishes its row, W row, score and squared norm
+      if (elig && j == bj) {
+        chosen = true;
+#pragma unroll
+        for (int q = 0; q < NW; q += 4) {
+          const uint4 v4 = make_uint4(w[q], w[q + 1], w[q + 2], w[q + 3]);
+          *reinterpret_cast<uint4 *>(&s_bc[buf][q]) = v4;
+          *reinterpret_cast<uint4 *>(&s_selrow[k][q]) = v4;
+        }
+        s_sel[k] = j;
+        s_sig[k] = sig;
+#pragma unroll
+        for (int m = 0; m < k; ++m) s_l[buf][m] = W[m];
+        s_gdiag[k] = row_self_dot<DT, NW>(w);
+      }
+      __syncthreads();
+      if (gm) {
+        float nl2 = 0.f, ly = 0.f;
+#pragma unroll
+        for (int m = 0; m < k; ++m) {
+          const float l = s_l[buf][m];
+          nl2 = fmaf(l, l, nl2);
+          ly = fmaf(l, s_y[m], ly);
+        }
+        const float alpha = fmaf(s_gdiag[k], 1.f + ridge_rel, ridge_abs);
+        const float Lkk = sqrtf(fmaxf(alpha - nl2, 1e-30f));
+        const float yk = (s_sig[k] - ly) / Lkk;
+        if (k + 1 < s) {
+          float acc = row_dot<DT, NW>(w, s_bc[buf]);
+#pragma unroll
+          for (int m = 0; m < k; ++m) acc = fmaf(-W[m], s_l[buf][m], acc);
+          W[k] = acc / Lkk;
+          rho = fmaf(-W[k], yk, rho);
+        }
+        if (tid == 0) {
+#pragma unroll
+          for (int m = 0; m < k; ++m) s_L[k * SMAX + m] = s_l[buf][m];
+          s_L[k * SMAX + k] = Lkk;
+          s_y[k] = yk;
+        }
+      }
     }
   }
   __syncthreads();
@@ -242,14 +309,11 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
   }
   __syncthreads();
 
-  // residual r = x - D_S^T c from the stored atoms
+  // residual r = x - D_S^T c from the chosen rows
   float rr = 0.f, xx = 0.f;
   for (int i = tid; i < D; i += blockDim.x) {
     float r = s_x[i];
-    for (int k = 0; k < s; ++k) {
-      const int jk = s_sel[k] < N ? s_sel[k] : N - 1;
-      r = fmaf(-s_c[k], elem_f<DT>(dict_atoms + (size_t)jk * ROWB, i), r);
-    }
+    for (int k = 0; k < s; ++k) r = fmaf(-s_c[k], lds_elem<DT>(s_selrow[k], i), r);
     rr = fmaf(r, r, rr);
     xx = fmaf(s_x[i], s_x[i], xx);
   }
@@ -278,7 +342,7 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
 
 #define FADKV_SEL_INST(DT, D, SM)                                                                 \
   template __global__ void select_kernel<DT, D, SM>(                                             \
-      const uint8_t *, const uint8_t *, int, int, int, int, int, float, float, float, float,    \
+      const uint8_t *, const uint8_t *, int, int, int, int, int, int, float, float, float, float, \
       const uint16_t *, const float *, const uint8_t *, int32_t *, float *, float *, uint8_t *);
 #define FADKV_SEL_INST_D(DT, D) FADKV_SEL_INST(DT, D, 8) FADKV_SEL_INST(DT, D, 16) FADKV_SEL_INST(DT, D, 32)
 FADKV_SEL_INST_D(DT_F32, 64)
@@ -298,7 +362,7 @@ hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int
   const uint8_t *A = static_cast<const uint8_t *>(atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
 #define L(DT, D, SM)                                                                              \
-  hipLaunchKernelGGL((select_kernel<DT, D, SM>), grid, block, 0, stream, A, Xb, N, M, n, s, select, \
+  hipLaunchKernelGGL((select_kernel<DT, D, SM>), grid, block, 0, stream, A, Xb, num_dicts, N, M, n, s, select, \
                      ridge_abs, ridge_rel, delta_key, delta_value, pool_idx, pool_sig, vstat, idx, \
                      coef, relerr, flags)
 #define LS(DT, D) \
