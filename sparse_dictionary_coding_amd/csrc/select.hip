@@ -18,9 +18,10 @@
 // Finally r = x - D_S^T c is formed from the chosen rows and e = ||r|| / ||x||.
 //
 // Each step costs two workgroup barriers: (1) after every wave has published its local
-// argmax (wave reduction through DPP), (2) after the winner has published its row, its W row
-// and its diagonal.  The LDS slots they use are double-buffered by step parity, so no third
-// barrier is needed before they are rewritten.
+// argmax (wave reduction through DPP), (2) after the winner has published its W row, score
+// and squared norm.  The winning row itself is read by every wave through the scalar cache.
+// The LDS slots are double-buffered by step parity, so no third barrier is needed before they
+// are rewritten.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +30,6 @@ namespace fadkv {
 namespace {
 constexpr int MAX_THREADS = 512;
 constexpr int MAX_WAVES = MAX_THREADS / 64;
-constexpr int STAGE_ROWS = 16;
 }  // namespace
 
 template <int DT, int D> struct RowWords {
@@ -37,25 +37,25 @@ template <int DT, int D> struct RowWords {
   static constexpr int ROWB = D * Elem<DT>::bytes;
 };
 
+// Dot product of the thread's row with a row every lane reads at the same address.  The address
+// is wave-uniform and the atoms are read-only in this kernel, so the compiler fetches that row
+// with scalar loads and feeds it to v_dot2 as the scalar operand: no LDS broadcast and no
+// vector registers for the shared row.
 template <int DT, int NW>
-__device__ __forceinline__ float row_dot(const uint32_t (&a)[NW], const uint32_t *__restrict__ b) {
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+__device__ __forceinline__ float row_dot_uniform(const uint32_t (&a)[NW],
+                                                 const uint32_t *__restrict__ row) {
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int q = 0; q < NW; q += 4) {
-    const uint4 bb = *reinterpret_cast<const uint4 *>(b + q);
+  for (int q = 0; q < NW; q += 2) {
     if constexpr (DT == DT_F32) {
-      s0 = fmaf(__uint_as_float(a[q + 0]), __uint_as_float(bb.x), s0);
-      s1 = fmaf(__uint_as_float(a[q + 1]), __uint_as_float(bb.y), s1);
-      s2 = fmaf(__uint_as_float(a[q + 2]), __uint_as_float(bb.z), s2);
-      s3 = fmaf(__uint_as_float(a[q + 3]), __uint_as_float(bb.w), s3);
+      s0 = fmaf(__uint_as_float(a[q]), __uint_as_float(row[q]), s0);
+      s1 = fmaf(__uint_as_float(a[q + 1]), __uint_as_float(row[q + 1]), s1);
     } else {
-      s0 = dot2<DT>(a[q + 0], bb.x, s0);
-      s1 = dot2<DT>(a[q + 1], bb.y, s1);
-      s2 = dot2<DT>(a[q + 2], bb.z, s2);
-      s3 = dot2<DT>(a[q + 3], bb.w, s3);
+      s0 = dot2<DT>(a[q], row[q], s0);
+      s1 = dot2<DT>(a[q + 1], row[q + 1], s1);
     }
   }
-  return (s0 + s1) + (s2 + s3);
+  return s0 + s1;
 }
 
 template <int DT, int NW>
@@ -89,7 +89,6 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
     float *__restrict__ out_relerr, uint8_t *__restrict__ out_flags) {
   constexpr int NW = RowWords<DT, D>::NW;
   constexpr int ROWB = RowWords<DT, D>::ROWB;
-  __shared__ __attribute__((aligned(16))) uint32_t s_bc[2][NW];        // winner's row, by parity
   __shared__ __attribute__((aligned(16))) uint32_t s_selrow[SMAX][NW];  // chosen rows
   __shared__ float s_x[D];
   __shared__ float s_L[SMAX * SMAX];
@@ -99,8 +98,6 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
   __shared__ float s_rv[2][MAX_WAVES];
   __shared__ int s_rj[2][MAX_WAVES];
   __shared__ float s_sum[2][MAX_WAVES];
-  // per-wave staging of STAGE_ROWS rows, one 16-byte pad per row against bank conflicts
-  __shared__ __attribute__((aligned(16))) uint32_t s_stage[MAX_WAVES][STAGE_ROWS * (ROWB / 4 + 4)];
 
   // With a multiple of 8 dictionaries, workgroup i (dispatched to XCD i % 8) takes a vector of
   // dictionary xcd + 8 * (r / M), r = i / 8: each dictionary's pool rows are gathered through
@@ -140,44 +137,17 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
     j = jj < N ? jj : N - 1;   // the screening kernel writes indices < N; never read past the set
     sig = pool_sig[gv * n + tid];
   }
-  // Gather the pool rows with whole-row coalesced loads: CPR lanes cover one row (16 bytes
-  // each), so a wave instruction reads 64/CPR complete rows; rows pass through a per-wave LDS
-  // stage of 16 rows and each thread then takes its own row from there.
+  // each thread loads its own pool row (all 16-byte loads issued back to back)
   uint32_t w[NW];
   {
-    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;           // rows per wave instruction
-    uint4 *stage = reinterpret_cast<uint4 *>(s_stage[wave]);
-    const int base_row = wave * 64;
+    const uint4 *src = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)(act ? j : 0) * ROWB);
 #pragma unroll
-    for (int g = 0; g < 64 / STAGE_ROWS; ++g) {
-#pragma unroll
-      for (int i = 0; i < STAGE_ROWS / RPI; ++i) {
-        const int r = g * STAGE_ROWS + i * RPI + lane / CPR;   // row within this wave's 64
-        const int t = base_row + r;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < n) {
-          int jr = pool_idx[gv * n + t];
-          jr = jr < N ? jr : N - 1;
-          v = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)jr * ROWB)[lane % CPR];
-        }
-        stage[(i * RPI + lane / CPR) * (CPR + 1) + lane % CPR] = v;
-      }
-      // same wave wrote the stage: LDS operations of one wave complete in order
-      if (lane / STAGE_ROWS == g) {
-        const int r = lane % STAGE_ROWS;
-#pragma unroll
-        for (int q = 0; q < NW / 4; ++q) {
-          const uint4 v = stage[r * (CPR + 1) + q];
-          w[4 * q + 0] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-        }
-      }
-    }
-    if (!act) {
-#pragma unroll
-      for (int q = 0; q < NW; ++q) w[q] = 0u;
+    for (int q = 0; q < NW / 4; ++q) {
+      const uint4 v = act ? src[q] : make_uint4(0, 0, 0, 0);
+      w[4 * q + 0] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
     }
   }
+  const float gself = row_self_dot<DT, NW>(w);   // ||d_j||^2, needed if this row is chosen
   for (int i = tid; i < D; i += blockDim.x) s_x[i] = elem_f<DT>(X + gv * ROWB, i);
   if (tid < SMAX) s_sel[tid] = 0;   // every slot names a valid row even if no thread wins
 
@@ -215,21 +185,17 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
           bj = qj;
         }
       }
-      // (2) the winner publishes its row, W row, score and squared norm
+      // (2) the winner publishes its W row, score and squared norm; every wave fetches the
+      // winning row itself through the scalar cache
+      const int jstar = __builtin_amdgcn_readfirstlane(bj);
       if (elig && j == bj) {
         chosen = true;
-#pragma unroll
-        for (int q = 0; q < NW; q += 4) {
-          const uint4 v4 = make_uint4(w[q], w[q + 1], w[q + 2], w[q + 3]);
-          *reinterpret_cast<uint4 *>(&s_bc[buf][q]) = v4;
-          *reinterpret_cast<uint4 *>(&s_selrow[k][q]) = v4;
-        }
-        s_sel[k] = j;
         s_sig[k] = sig;
 #pragma unroll
         for (int m = 0; m < k; ++m) s_l[buf][m] = W[m];
-        s_gdiag[k] = row_self_dot<DT, NW>(w);
+        s_gdiag[k] = gself;
       }
+      if (tid == 0) s_sel[k] = jstar;
       __syncthreads();
       if (gm) {
         float nl2 = 0.f, ly = 0.f;
@@ -243,7 +209,8 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
         const float Lkk = sqrtf(fmaxf(alpha - nl2, 1e-30f));
         const float yk = (s_sig[k] - ly) / Lkk;
         if (k + 1 < s) {
-          float acc = row_dot<DT, NW>(w, s_bc[buf]);
+          const uint32_t *row = reinterpret_cast<const uint32_t *>(dict_atoms + (size_t)jstar * ROWB);
+          float acc = row_dot_uniform<DT, NW>(w, row);
 #pragma unroll
           for (int m = 0; m < k; ++m) acc = fmaf(-W[m], s_l[buf][m], acc);
           W[k] = acc / Lkk;
@@ -257,6 +224,13 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
         }
       }
     }
+  }
+  __syncthreads();
+  // the chosen rows, for PL's Gram matrix and the residual
+  for (int e = tid; e < s * (NW / 4); e += blockDim.x) {
+    const int k = e / (NW / 4), c = e % (NW / 4);
+    reinterpret_cast<uint4 *>(s_selrow[k])[c] =
+        reinterpret_cast<const uint4 *>(dict_atoms + (size_t)s_sel[k] * ROWB)[c];
   }
   __syncthreads();
 
