@@ -164,7 +164,8 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
       const int buf = k & 1;
       // (1) wave argmax of |rho| over unchosen entries, ties to the lowest atom index
       const bool elig = act && !chosen;
-      const float v = elig ? fabsf(rho) : -1.f;
+      float v = elig ? fabsf(rho) : -1.f;
+      v = v != v ? 0.f : v;   // a NaN score (non-finite atoms) ranks as 0, never above real ones
       const float wmax = wave_max_f32(v);
       const unsigned long long hit = __ballot(elig && v == wmax);
       int wj;
@@ -187,7 +188,10 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
       }
       // (2) the winner publishes its W row, score and squared norm; every wave fetches the
       // winning row itself through the scalar cache
-      const int jstar = __builtin_amdgcn_readfirstlane(bj);
+      // bj names an eligible pool row whenever the block has one; the clamp keeps the row
+      // address inside the dictionary whatever the pool holds
+      int jstar = __builtin_amdgcn_readfirstlane(bj);
+      jstar = jstar < 0 ? 0 : (jstar >= N ? N - 1 : jstar);
       if (elig && j == bj) {
         chosen = true;
         s_sig[k] = sig;

@@ -132,6 +132,37 @@ def test_encode_edge_cases():
     rep.check()
 
 
+def test_select_is_bounded_for_any_pool_and_non_finite_atoms():
+    """Regression: NaN scores once let the greedy argmax name no row (index 0x7fffffff).  Now
+    every output index stays in [0, N) whatever the pool holds (indices past N, NaN and Inf
+    scores) and whatever the atoms hold (NaN/Inf rows)."""
+    _banner("bounded selection on garbage pools")
+    rng = np.random.default_rng(9)
+    T, N, d, M, n, s = 2, 300, 128, 40, 64, 8
+    A = torch.from_numpy(rng.standard_normal((T, N, d)).astype(np.float32)).to(torch.float16)
+    A[0, 5] = float("nan")
+    A[1, 7] = float("inf")
+    X = torch.from_numpy(rng.standard_normal((T, M, d)).astype(np.float32)).to(torch.float16)
+    At, Xt = A.to(DEV), X.to(DEV)
+    for select in ("gm", "pl"):
+        p = fadkv.Params(n=n, s=s, select=select)
+        codes = fadkv.fadkv_encode(At, Xt, p)
+        torch.cuda.synchronize()
+        gi = codes.idx.cpu().numpy()
+        assert np.all((gi >= -1) & (gi < N))
+        pool = fadkv.Pool.empty(T, M, n, DEV)
+        pool.idx.copy_(torch.from_numpy(rng.integers(-32768, 32767, (T, M, n)).astype(np.int16)))
+        sc = rng.standard_normal((T, M, n)).astype(np.float32)
+        sc[0, :, :] = np.nan
+        sc[1, ::2, :] = np.inf
+        pool.score.copy_(torch.from_numpy(sc))
+        pool.status.zero_()
+        codes = fadkv.fadkv_select_support(At, Xt, p, pool)
+        torch.cuda.synchronize()
+        gi = codes.idx.cpu().numpy()
+        assert np.all((gi >= 0) & (gi < N))
+
+
 def test_encode_is_deterministic():
     _banner("determinism")
     w = small("f16", 128, 2048, 256, 8, 200, T=4, aniso=True)
