@@ -17,20 +17,17 @@
 // PL takes the s largest |sigma| of the pool the same way (no rho update) and solves once.
 // Finally r = x - D_S^T c is formed from the chosen rows and e = ||r|| / ||x||.
 //
-// Each step costs two workgroup barriers: (1) after every wave has published its local
-// argmax (wave reduction through DPP), (2) after the winner has published its W row, score
-// and squared norm.  The winning row itself is read by every wave through the scalar cache.
-// The LDS slots are double-buffered by step parity, so no third barrier is needed before they
-// are rewritten.
+// One workgroup barrier per step.  Before it, every wave reduces its own argmax (DPP) and its
+// candidate lane publishes a 64-bit key (|rho| bits, 0xFFFF - atom, wave) together with its
+// W row, score and squared norm.  After it, every wave takes the largest key, which names the
+// winning atom and the wave whose slot holds the winner's data; the winning row itself is
+// read by every wave through the scalar cache.  The slots are double-buffered by step parity:
+// a slot written at step k + 2 is written after the barrier of step k + 1, which every reader
+// of step k has passed.  After the last step a single wave forms c and the residual.
 #include "common.h"
 #include "kernels.h"
 
 namespace fadkv {
-
-namespace {
-constexpr int MAX_THREADS = 512;
-constexpr int MAX_WAVES = MAX_THREADS / 64;
-}  // namespace
 
 template <int DT, int D> struct RowWords {
   static constexpr int NW = DT == DT_F32 ? D : D / 2;   // 32-bit words per atom row
@@ -80,8 +77,9 @@ template <int DT> __device__ __forceinline__ float lds_elem(const uint32_t *row,
   else return (i & 1) ? hi_f<DT>(row[i >> 1]) : lo_f<DT>(row[i >> 1]);
 }
 
-template <int DT, int D, int SMAX>
-__global__ __launch_bounds__(MAX_THREADS) void select_kernel(
+// 16-bit rows with s <= 16 fit 128 VGPRs: 4 waves per SIMD, two 8-wave workgroups per CU.
+template <int DT, int D, int SMAX, int MAXW>
+__global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) void select_kernel(
     const uint8_t *__restrict__ atoms, const uint8_t *__restrict__ X, int num_dicts, int N, int M,
     int n, int s, int select, float ridge_abs, float ridge_rel, float delta_key, float delta_value,
     const uint16_t *__restrict__ pool_idx, const float *__restrict__ pool_sig,
@@ -89,15 +87,13 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
     float *__restrict__ out_relerr, uint8_t *__restrict__ out_flags) {
   constexpr int NW = RowWords<DT, D>::NW;
   constexpr int ROWB = RowWords<DT, D>::ROWB;
+  constexpr int PUB = SMAX + 2;   // published slot: W row, score, squared norm
   __shared__ __attribute__((aligned(16))) uint32_t s_selrow[SMAX][NW];  // chosen rows
-  __shared__ float s_x[D];
-  __shared__ float s_L[SMAX * SMAX];
-  __shared__ float s_y[SMAX], s_c[SMAX], s_sig[SMAX], s_gdiag[SMAX];
-  __shared__ float s_l[2][SMAX];
+  __shared__ float s_L[SMAX * SMAX];   // row k: l of step k (strictly lower part of L)
+  __shared__ float s_linv[SMAX], s_y[SMAX], s_sig[SMAX], s_c[SMAX];
   __shared__ int s_sel[SMAX];
-  __shared__ float s_rv[2][MAX_WAVES];
-  __shared__ int s_rj[2][MAX_WAVES];
-  __shared__ float s_sum[2][MAX_WAVES];
+  __shared__ unsigned long long s_key[2][MAXW];
+  __shared__ float s_pub[2][MAXW][PUB];
 
   // With a multiple of 8 dictionaries, workgroup i (dispatched to XCD i % 8) takes a vector of
   // dictionary xcd + 8 * (r / M), r = i / 8: each dictionary's pool rows are gathered through
@@ -127,10 +123,12 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
     }
     return;
   }
+  // key slots of absent waves read as "no candidate" (no present wave writes them)
+  if (tid < 2 * MAXW && tid % MAXW >= nwaves) s_key[tid / MAXW][tid % MAXW] = 0ull;
 
   const uint8_t *dict_atoms = atoms + (size_t)dict * N * ROWB;
   const bool act = tid < n;
-  int j = 0x7fffffff;
+  int j = 0;
   float sig = 0.f;
   if (act) {
     const int jj = pool_idx[gv * n + tid];
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
   // each thread loads its own pool row (all 16-byte loads issued back to back)
   uint32_t w[NW];
   {
-    const uint4 *src = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)(act ? j : 0) * ROWB);
+    const uint4 *src = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)j * ROWB);
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
       const uint4 v = act ? src[q] : make_uint4(0, 0, 0, 0);
@@ -148,129 +146,150 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
     }
   }
   const float gself = row_self_dot<DT, NW>(w);   // ||d_j||^2, needed if this row is chosen
-  for (int i = tid; i < D; i += blockDim.x) s_x[i] = elem_f<DT>(X + gv * ROWB, i);
-  if (tid < SMAX) s_sel[tid] = 0;   // every slot names a valid row even if no thread wins
+  // wave 0 keeps x (elements lane and lane + 64) for the residual
+  float x0 = 0.f, x1 = 0.f;
+  if (wave == 0) {
+    const uint8_t *xr = X + gv * ROWB;
+    if (lane < D) x0 = elem_f<DT>(xr, lane);
+    if (D > 64) x1 = elem_f<DT>(xr, lane + 64);
+  }
 
   const bool gm = select == 0;
   float rho = sig;
-  float W[SMAX];
+  float W[SMAX], Y[SMAX];   // Y: y, the same in every lane
 #pragma unroll
-  for (int m = 0; m < SMAX; ++m) W[m] = 0.f;
+  for (int m = 0; m < SMAX; ++m) W[m] = Y[m] = 0.f;
   bool chosen = false;
 
 #pragma unroll
   for (int k = 0; k < SMAX; ++k) {
     if (k < s) {
       const int buf = k & 1;
-      // (1) wave argmax of |rho| over unchosen entries, ties to the lowest atom index
+      // wave argmax of |rho| over unchosen entries, ties to the lowest atom index
       const bool elig = act && !chosen;
       float v = elig ? fabsf(rho) : -1.f;
       v = v != v ? 0.f : v;   // a NaN score (non-finite atoms) ranks as 0, never above real ones
-      const float wmax = wave_max_f32(v);
-      const unsigned long long hit = __ballot(elig && v == wmax);
-      int wj;
-      if (__popcll(hit) == 1) wj = __builtin_amdgcn_readlane(j, (int)__ffsll((long long)hit) - 1);
-      else wj = wave_min_i32((elig && v == wmax) ? j : 0x7fffffff);
-      if (lane == 0) {
-        s_rv[buf][wave] = wmax;
-        s_rj[buf][wave] = wj;
+      const float wmax = wave_max_f32_l63(v);
+      const bool top = elig && v == wmax;
+      const unsigned long long hit = __ballot(top);
+      int cl = hit ? (int)__ffsll((long long)hit) - 1 : 0;
+      if (__popcll(hit) > 1) {
+        const int wj = wave_min_i32(top ? j : 0x7fffffff);
+        cl = (int)__ffsll((long long)__ballot(top && j == wj)) - 1;
       }
-      __syncthreads();
-      float bv = s_rv[buf][0];
-      int bj = s_rj[buf][0];
-      for (int q = 1; q < nwaves; ++q) {
-        const float qv = s_rv[buf][q];
-        const int qj = s_rj[buf][q];
-        if (qv > bv || (qv == bv && qj < bj)) {
-          bv = qv;
-          bj = qj;
-        }
-      }
-      // (2) the winner publishes its W row, score and squared norm; every wave fetches the
-      // winning row itself through the scalar cache
-      // bj names an eligible pool row whenever the block has one; the clamp keeps the row
-      // address inside the dictionary whatever the pool holds
-      int jstar = __builtin_amdgcn_readfirstlane(bj);
-      jstar = jstar < 0 ? 0 : (jstar >= N ? N - 1 : jstar);
-      if (elig && j == bj) {
-        chosen = true;
-        s_sig[k] = sig;
+      const int jc = __builtin_amdgcn_readlane(j, cl);
+      const unsigned long long key =
+          hit ? ((unsigned long long)__float_as_uint(wmax) << 32) |
+                    ((unsigned)(0xFFFF - jc) << 8) | (unsigned)wave
+              : 0ull;
+      if (lane == cl) {
+        s_key[buf][wave] = key;
 #pragma unroll
-        for (int m = 0; m < k; ++m) s_l[buf][m] = W[m];
-        s_gdiag[k] = gself;
+        for (int m = 0; m < k; ++m) s_pub[buf][wave][m] = W[m];
+        s_pub[buf][wave][SMAX] = sig;
+        s_pub[buf][wave][SMAX + 1] = gself;
       }
-      if (tid == 0) s_sel[k] = jstar;
       __syncthreads();
+      unsigned long long best = s_key[buf][0];
+#pragma unroll
+      for (int q = 1; q < MAXW; ++q) {
+        const unsigned long long kq = s_key[buf][q];
+        best = kq > best ? kq : best;
+      }
+      const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)best);
+      const int bw = (int)(lo & (MAXW - 1));
+      // a key names an eligible pool row whenever the block has one; the clamp keeps the row
+      // address inside the dictionary whatever the pool holds
+      int jstar = 0xFFFF - (int)((lo >> 8) & 0xFFFFu);
+      jstar = jstar >= N ? N - 1 : jstar;
+      if (elig && j == jstar) {
+        chosen = true;
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q)
+          reinterpret_cast<uint4 *>(s_selrow[k])[q] =
+              make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+      }
+      const float sigk = s_pub[buf][bw][SMAX];
       if (gm) {
+        float l[SMAX];
         float nl2 = 0.f, ly = 0.f;
 #pragma unroll
         for (int m = 0; m < k; ++m) {
-          const float l = s_l[buf][m];
-          nl2 = fmaf(l, l, nl2);
-          ly = fmaf(l, s_y[m], ly);
+          l[m] = s_pub[buf][bw][m];
+          nl2 = fmaf(l[m], l[m], nl2);
+          ly = fmaf(l[m], Y[m], ly);
         }
-        const float alpha = fmaf(s_gdiag[k], 1.f + ridge_rel, ridge_abs);
-        const float Lkk = sqrtf(fmaxf(alpha - nl2, 1e-30f));
-        const float yk = (s_sig[k] - ly) / Lkk;
+        const float alpha = fmaf(s_pub[buf][bw][SMAX + 1], 1.f + ridge_rel, ridge_abs);
+        const float invL = __builtin_amdgcn_rsqf(fmaxf(alpha - nl2, 1e-30f));
+        // y is the same in every lane: keep it in scalar registers
+        const float yk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int((sigk - ly) * invL)));
+        Y[k] = yk;
         if (k + 1 < s) {
           const uint32_t *row = reinterpret_cast<const uint32_t *>(dict_atoms + (size_t)jstar * ROWB);
           float acc = row_dot_uniform<DT, NW>(w, row);
 #pragma unroll
-          for (int m = 0; m < k; ++m) acc = fmaf(-W[m], s_l[buf][m], acc);
-          W[k] = acc / Lkk;
+          for (int m = 0; m < k; ++m) acc = fmaf(-W[m], l[m], acc);
+          W[k] = acc * invL;
           rho = fmaf(-W[k], yk, rho);
         }
         if (tid == 0) {
 #pragma unroll
-          for (int m = 0; m < k; ++m) s_L[k * SMAX + m] = s_l[buf][m];
-          s_L[k * SMAX + k] = Lkk;
+          for (int m = 0; m < k; ++m) s_L[k * SMAX + m] = l[m];
+          s_linv[k] = invL;
           s_y[k] = yk;
         }
       }
-    }
-  }
-  __syncthreads();
-  // the chosen rows, for PL's Gram matrix and the residual
-  for (int e = tid; e < s * (NW / 4); e += blockDim.x) {
-    const int k = e / (NW / 4), c = e % (NW / 4);
-    reinterpret_cast<uint4 *>(s_selrow[k])[c] =
-        reinterpret_cast<const uint4 *>(dict_atoms + (size_t)s_sel[k] * ROWB)[c];
-  }
-  __syncthreads();
-
-  if (gm) {
-    if (tid == 0) {   // c = L^{-T} y
-      for (int i = s - 1; i >= 0; --i) {
-        float acc = s_y[i];
-        for (int m = i + 1; m < s; ++m) acc = fmaf(-s_L[m * SMAX + i], s_c[m], acc);
-        s_c[i] = acc / s_L[i * SMAX + i];
+      if (tid == 0) {
+        s_sel[k] = jstar;
+        s_sig[k] = sigk;
       }
     }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // ---- one wave: coefficients, residual, outputs ----
+  float c = 0.f;   // lane k < s holds c_k
+  if (gm) {
+    // c = L^{-T} y: lane m carries t_m = y_m - sum_{i > m} L_im c_i; column i is finished
+    // once every later column has been folded in, so c_i = t_i / L_ii is final at step i
+    float t = lane < s ? s_y[lane < SMAX ? lane : 0] : 0.f;
+    float lcol[SMAX];
+#pragma unroll
+    for (int i = 0; i < SMAX; ++i) lcol[i] = (i < s && lane < i) ? s_L[i * SMAX + lane] : 0.f;
+#pragma unroll
+    for (int i = SMAX - 1; i >= 0; --i) {
+      if (i < s) {
+        const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), i)) * s_linv[i];
+        t = fmaf(-lcol[i], ci, t);
+      }
+    }
+    c = lane < s ? t * s_linv[lane < SMAX ? lane : 0] : 0.f;
   } else {
-    // PL: G_SS from the chosen rows, then Cholesky and two triangular solves on thread 0
-    for (int e = tid; e < s * s; e += blockDim.x) {
-      const int r = e / s, c = e % s;
-      if (c > r) continue;
+    // PL: G_SS from the chosen rows, then Cholesky and two triangular solves on lane 0
+    for (int e = lane; e < s * s; e += 64) {
+      const int r = e / s, cc = e % s;
+      if (cc > r) continue;
       float acc = 0.f;
       for (int q = 0; q < NW; ++q) {
-        const uint32_t a = s_selrow[r][q], b = s_selrow[c][q];
+        const uint32_t a = s_selrow[r][q], b = s_selrow[cc][q];
         if constexpr (DT == DT_F32) acc = fmaf(__uint_as_float(a), __uint_as_float(b), acc);
         else acc = dot2<DT>(a, b, acc);
       }
-      s_L[r * SMAX + c] = acc;   // lower triangle of G_SS, factored in place below
+      s_L[r * SMAX + cc] = acc;   // lower triangle of G_SS, factored in place below
     }
-    __syncthreads();
-    if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (lane == 0) {
       for (int r = 0; r < s; ++r) s_L[r * SMAX + r] = fmaf(s_L[r * SMAX + r], 1.f + ridge_rel, ridge_abs);
-      for (int c = 0; c < s; ++c) {
-        float dcc = s_L[c * SMAX + c];
-        for (int m = 0; m < c; ++m) dcc = fmaf(-s_L[c * SMAX + m], s_L[c * SMAX + m], dcc);
+      for (int cc = 0; cc < s; ++cc) {
+        float dcc = s_L[cc * SMAX + cc];
+        for (int m = 0; m < cc; ++m) dcc = fmaf(-s_L[cc * SMAX + m], s_L[cc * SMAX + m], dcc);
         const float Lcc = sqrtf(fmaxf(dcc, 1e-30f));
-        s_L[c * SMAX + c] = Lcc;
-        for (int r = c + 1; r < s; ++r) {
-          float v = s_L[r * SMAX + c];
-          for (int m = 0; m < c; ++m) v = fmaf(-s_L[r * SMAX + m], s_L[c * SMAX + m], v);
-          s_L[r * SMAX + c] = v / Lcc;
+        s_L[cc * SMAX + cc] = Lcc;
+        for (int r = cc + 1; r < s; ++r) {
+          float v = s_L[r * SMAX + cc];
+          for (int m = 0; m < cc; ++m) v = fmaf(-s_L[r * SMAX + m], s_L[cc * SMAX + m], v);
+          s_L[r * SMAX + cc] = v / Lcc;
         }
       }
       for (int i = 0; i < s; ++i) {
@@ -284,45 +303,40 @@ __global__ __launch_bounds__(MAX_THREADS) void select_kernel(
         s_c[i] = acc / s_L[i * SMAX + i];
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    c = lane < s ? s_c[lane < SMAX ? lane : 0] : 0.f;
   }
-  __syncthreads();
 
-  // residual r = x - D_S^T c from the chosen rows
-  float rr = 0.f, xx = 0.f;
-  for (int i = tid; i < D; i += blockDim.x) {
-    float r = s_x[i];
-    for (int k = 0; k < s; ++k) r = fmaf(-s_c[k], lds_elem<DT>(s_selrow[k], i), r);
-    rr = fmaf(r, r, rr);
-    xx = fmaf(s_x[i], s_x[i], xx);
-  }
-  rr = wave_sum(rr);
-  xx = wave_sum(xx);
-  if (lane == 0) {
-    s_sum[0][wave] = rr;
-    s_sum[1][wave] = xx;
-  }
-  __syncthreads();
-  if (tid < s) {
-    out_idx[gv * s + tid] = s_sel[tid];
-    out_coef[gv * s + tid] = s_c[tid];
-  }
-  if (tid == 0) {
-    float R = 0.f, Xn = 0.f;
-    for (int q = 0; q < nwaves; ++q) {
-      R += s_sum[0][q];
-      Xn += s_sum[1][q];
+  // residual r = x - D_S^T c from the chosen rows; lane i holds elements i and i + 64
+  float r0 = x0, r1 = x1;
+#pragma unroll
+  for (int k = 0; k < SMAX; ++k) {
+    if (k < s) {
+      const float ck = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), k));
+      if (lane < D) r0 = fmaf(-ck, lds_elem<DT>(s_selrow[k], lane), r0);
+      if (D > 64) r1 = fmaf(-ck, lds_elem<DT>(s_selrow[k], lane + 64), r1);
     }
-    const float e = sqrtf(R / Xn);
+  }
+  const float rr = wave_sum(fmaf(r0, r0, r1 * r1));
+  const float xx = wave_sum(fmaf(x0, x0, x1 * x1));
+  if (lane < s) {
+    out_idx[gv * s + lane] = s_sel[lane < SMAX ? lane : 0];
+    out_coef[gv * s + lane] = c;
+  }
+  if (lane == 0) {
+    const float e = sqrtf(rr / xx);
     out_relerr[gv] = e;
     out_flags[gv] = e > delta ? FLAG_TRIGGER : 0;
   }
 }
 
-#define FADKV_SEL_INST(DT, D, SM)                                                                 \
-  template __global__ void select_kernel<DT, D, SM>(                                             \
+#define FADKV_SEL_INST(DT, D, SM, MW)                                                             \
+  template __global__ void select_kernel<DT, D, SM, MW>(                                         \
       const uint8_t *, const uint8_t *, int, int, int, int, int, int, float, float, float, float, \
       const uint16_t *, const float *, const uint8_t *, int32_t *, float *, float *, uint8_t *);
-#define FADKV_SEL_INST_D(DT, D) FADKV_SEL_INST(DT, D, 8) FADKV_SEL_INST(DT, D, 16) FADKV_SEL_INST(DT, D, 32)
+#define FADKV_SEL_INST_S(DT, D, SM) FADKV_SEL_INST(DT, D, SM, 4) FADKV_SEL_INST(DT, D, SM, 8)
+#define FADKV_SEL_INST_D(DT, D) \
+  FADKV_SEL_INST_S(DT, D, 8) FADKV_SEL_INST_S(DT, D, 16) FADKV_SEL_INST_S(DT, D, 32)
 FADKV_SEL_INST_D(DT_F32, 64)
 FADKV_SEL_INST_D(DT_F32, 128)
 FADKV_SEL_INST_D(DT_F16, 64)
@@ -336,21 +350,24 @@ hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int
                          const float *pool_sig, const uint8_t *vstat, int32_t *idx, float *coef,
                          float *relerr, uint8_t *flags, hipStream_t stream) {
   const size_t G = (size_t)num_dicts * M;
-  dim3 grid((unsigned)G), block((unsigned)(((n + 63) / 64) * 64));
+  const unsigned threads = (unsigned)(((n + 63) / 64) * 64);   // n <= 512: at most 8 waves
+  dim3 grid((unsigned)G), block(threads);
   const uint8_t *A = static_cast<const uint8_t *>(atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
-#define L(DT, D, SM)                                                                              \
-  hipLaunchKernelGGL((select_kernel<DT, D, SM>), grid, block, 0, stream, A, Xb, num_dicts, N, M, n, s, select, \
-                     ridge_abs, ridge_rel, delta_key, delta_value, pool_idx, pool_sig, vstat, idx, \
-                     coef, relerr, flags)
+#define L(DT, D, SM, MW)                                                                          \
+  hipLaunchKernelGGL((select_kernel<DT, D, SM, MW>), grid, block, 0, stream, A, Xb, num_dicts, N, \
+                     M, n, s, select, ridge_abs, ridge_rel, delta_key, delta_value, pool_idx,      \
+                     pool_sig, vstat, idx, coef, relerr, flags)
+#define LW(DT, D, SM) do { if (threads <= 256) L(DT, D, SM, 4); else L(DT, D, SM, 8); } while (0)
 #define LS(DT, D) \
-  do { if (s <= 8) L(DT, D, 8); else if (s <= 16) L(DT, D, 16); else L(DT, D, 32); } while (0)
+  do { if (s <= 8) LW(DT, D, 8); else if (s <= 16) LW(DT, D, 16); else LW(DT, D, 32); } while (0)
 #define LD(DT) do { if (d == 64) LS(DT, 64); else LS(DT, 128); } while (0)
   if (dtype == DT_F32) LD(DT_F32);
   else if (dtype == DT_F16) LD(DT_F16);
   else LD(DT_BF16);
 #undef LD
 #undef LS
+#undef LW
 #undef L
   return hipGetLastError();
 }
