@@ -137,18 +137,21 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
-// Same reduction, finished inside the vector unit: after the row patterns, row_bcast:15 (into
-// rows 1 and 3) and row_bcast:31 (into rows 2 and 3) fold the four row maxima into lane 63.
-__device__ __forceinline__ float wave_max_f32_l63(float v) {
-  v = fmaxf(v, __int_as_float(dpp_i<0xB1>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_i<0x4E>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_i<0x141>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_i<0x140>(__float_as_int(v))));
-  const int b15 = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false);
-  v = fmaxf(v, __int_as_float(b15));
-  const int b31 = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false);
-  v = fmaxf(v, __int_as_float(b31));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+// Maximum over the wave of non-negative floats (negative values only as "absent"), in lane 63:
+// signed-integer max on the bit patterns orders such values like the floats.  Each level is
+// one DPP-fused v_max_i32 (the moved-in value defaults to INT_MIN, the identity): row-internal
+// patterns first, then row_bcast:15 (into rows 1 and 3) and row_bcast:31 (into rows 2 and 3).
+template <int CTRL, int ROWS = 0xF> __device__ __forceinline__ int max_dpp_i(int v) {
+  return max(v, __builtin_amdgcn_update_dpp((int)0x80000000, v, CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ int wave_max_nonneg_bits(int v) {
+  v = max_dpp_i<0xB1>(v);
+  v = max_dpp_i<0x4E>(v);
+  v = max_dpp_i<0x141>(v);
+  v = max_dpp_i<0x140>(v);
+  v = max_dpp_i<0x142, 0xA>(v);
+  v = max_dpp_i<0x143, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_min_i32(int v) {
   v = min(v, dpp_i<0xB1>(v));

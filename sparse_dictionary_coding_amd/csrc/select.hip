@@ -98,15 +98,19 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
   // With a multiple of 8 dictionaries, workgroup i (dispatched to XCD i % 8) takes a vector of
   // dictionary xcd + 8 * (r / M), r = i / 8: each dictionary's pool rows are gathered through
   // one XCD's L2.
-  size_t gv;
+  // (32-bit arithmetic: the grid has num_dicts * M < 2^32 workgroups)
+  const unsigned bid = blockIdx.x, uM = (unsigned)M;
+  unsigned dict_u, vec_u;
   if ((num_dicts & 7) == 0) {
-    const size_t r = blockIdx.x / 8;
-    const int xcd = blockIdx.x % 8;
-    gv = (size_t)(xcd + 8 * (int)(r / (size_t)M)) * M + r % (size_t)M;
+    const unsigned r = bid / 8u;
+    dict_u = bid % 8u + 8u * (r / uM);
+    vec_u = r % uM;
   } else {
-    gv = blockIdx.x;
+    dict_u = bid / uM;
+    vec_u = bid % uM;
   }
-  const int dict = (int)(gv / (size_t)M);
+  const int dict = __builtin_amdgcn_readfirstlane((int)dict_u);
+  const size_t gv = (size_t)dict * M + __builtin_amdgcn_readfirstlane(vec_u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
   const float delta = (dict & 1) ? delta_value : delta_key;
@@ -135,13 +139,14 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
     j = jj < N ? jj : N - 1;   // the screening kernel writes indices < N; never read past the set
     sig = pool_sig[gv * n + tid];
   }
-  // each thread loads its own pool row (all 16-byte loads issued back to back)
+  // each thread loads its own pool row (all 16-byte loads issued back to back); a thread past
+  // the pool loads row 0, which it never offers as a candidate
   uint32_t w[NW];
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(dict_atoms + (size_t)j * ROWB);
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
-      const uint4 v = act ? src[q] : make_uint4(0, 0, 0, 0);
+      const uint4 v = src[q];
       w[4 * q + 0] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
     }
   }
@@ -169,18 +174,18 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
       const bool elig = act && !chosen;
       float v = elig ? fabsf(rho) : -1.f;
       v = v != v ? 0.f : v;   // a NaN score (non-finite atoms) ranks as 0, never above real ones
-      const float wmax = wave_max_f32_l63(v);
-      const bool top = elig && v == wmax;
-      const unsigned long long hit = __ballot(top);
+      const int wmax = wave_max_nonneg_bits(__float_as_int(v));
+      const bool top = elig && __float_as_int(v) == wmax;
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(top);
       int cl = hit ? (int)__ffsll((long long)hit) - 1 : 0;
       if (__popcll(hit) > 1) {
         const int wj = wave_min_i32(top ? j : 0x7fffffff);
-        cl = (int)__ffsll((long long)__ballot(top && j == wj)) - 1;
+        cl = (int)__ffsll((long long)__builtin_amdgcn_ballot_w64(top && j == wj)) - 1;
       }
       const int jc = __builtin_amdgcn_readlane(j, cl);
       const unsigned long long key =
-          hit ? ((unsigned long long)__float_as_uint(wmax) << 32) |
-                    ((unsigned)(0xFFFF - jc) << 8) | (unsigned)wave
+          hit ? ((unsigned long long)(unsigned)wmax << 32) | ((unsigned)(0xFFFF - jc) << 8) |
+                    (unsigned)wave
               : 0ull;
       if (lane == cl) {
         s_key[buf][wave] = key;
@@ -202,31 +207,37 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
       // address inside the dictionary whatever the pool holds
       int jstar = 0xFFFF - (int)((lo >> 8) & 0xFFFFu);
       jstar = jstar >= N ? N - 1 : jstar;
-      if (elig && j == jstar) {
-        chosen = true;
+      const bool win = elig && j == jstar;
+      chosen = chosen || win;
+      float l[SMAX];
+#pragma unroll
+      for (int m = 0; m < k; ++m) l[m] = s_pub[buf][bw][m];
+      const float sigk = s_pub[buf][bw][SMAX];
+      const float gk = s_pub[buf][bw][SMAX + 1];
+      // G_{j,j*} for this thread's row: the winning row comes through the scalar cache while
+      // the published slot is read
+      float acc = 0.f;
+      if (gm && k + 1 < s)
+        acc = row_dot_uniform<DT, NW>(w, reinterpret_cast<const uint32_t *>(dict_atoms + (size_t)jstar * ROWB));
+      if (win) {
 #pragma unroll
         for (int q = 0; q < NW / 4; ++q)
           reinterpret_cast<uint4 *>(s_selrow[k])[q] =
               make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
       }
-      const float sigk = s_pub[buf][bw][SMAX];
       if (gm) {
-        float l[SMAX];
         float nl2 = 0.f, ly = 0.f;
 #pragma unroll
         for (int m = 0; m < k; ++m) {
-          l[m] = s_pub[buf][bw][m];
           nl2 = fmaf(l[m], l[m], nl2);
           ly = fmaf(l[m], Y[m], ly);
         }
-        const float alpha = fmaf(s_pub[buf][bw][SMAX + 1], 1.f + ridge_rel, ridge_abs);
+        const float alpha = fmaf(gk, 1.f + ridge_rel, ridge_abs);
         const float invL = __builtin_amdgcn_rsqf(fmaxf(alpha - nl2, 1e-30f));
         // y is the same in every lane: keep it in scalar registers
         const float yk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int((sigk - ly) * invL)));
         Y[k] = yk;
         if (k + 1 < s) {
-          const uint32_t *row = reinterpret_cast<const uint32_t *>(dict_atoms + (size_t)jstar * ROWB);
-          float acc = row_dot_uniform<DT, NW>(w, row);
 #pragma unroll
           for (int m = 0; m < k; ++m) acc = fmaf(-W[m], l[m], acc);
           W[k] = acc * invL;
