@@ -1,23 +1,28 @@
 // Screening scores and exact Top-n candidate pool (FAD-KV abstract and Figure 1: one pass of
 // dictionary correlations, then a one-shot Top-n pool by |score|, ties to the lowest index).
 //
-// One workgroup = 8 waves = one dictionary x 32 vectors.  The 32 vectors are the B operand of
-// v_mfma_f32_32x32x{16,2}: they stay in registers for the whole dictionary sweep.  Each wave
-// streams its own 32-atom tiles (A operand) from global memory/L2, loading the next tile's
-// fragment while the current one is scored; a tile's 32x32 fp32 scores land in 16 accumulators
-// per lane, all belonging to the lane's vector (column lane % 32), so every score is handled by
-// the lane that owns its vector.  Workgroups are numbered so that all workgroups of one
-// dictionary land on the same XCD (dispatch is round-robin over the 8 XCDs).
+// One workgroup = 8 waves = one dictionary x 32 vectors.  The 32 vectors are the B operands of
+// v_mfma_f32_16x16x32 (two blocks of 16 vectors) and stay in registers for the whole sweep.
+// Each wave streams its own 16-atom tiles.  A tile is copied global -> LDS by direct-to-LDS
+// loads whose lanes read the rows contiguously (one load moves 1 KB, four lanes a 64-byte
+// segment), then every lane reads its MFMA fragment (row lane % 16, 16-byte chunk
+// 4 i + lane / 16) back from the wave's stage.  The stage keeps chunk c of row r at position
+// c ^ swz(r), so the 16 rows of a fragment read fall in distinct LDS banks.  A tile's 16x16
+// scores per block land as 4 accumulators per lane: vector lane % 16 of the block, atoms
+// 4 (lane / 16) + e.  Workgroups are numbered so that all workgroups of one dictionary run on
+// the same XCD (dispatch is round-robin over the 8 XCDs).
 //
 // Selection is an exact radix select on the 47-bit key K = (bits(|score|) << 16) |
 // (0xFFFF - atom): larger K = larger |score|, then lower index, and every K is unique.
-//   sweep 1: histogram of |score| in 512 bins of 1/32 octave below ~1.5 ||x|| (two 16-bit
-//            counters per LDS word); the bin holding the n-th largest key is the boundary;
+//   sweep 1: histogram of |score| in 256 bins of 1/32 octave below ~1.5 ||x||; the bin
+//            holding the n-th largest key is the boundary;
 //   sweep 2: keys above the boundary bin go straight to the pool, keys inside it go to an LDS
 //            buffer of CAP entries from which the `need` largest keys are taken.
 // A vector whose boundary bin holds more than CAP keys is refined by further sweeps that
 // histogram its key range uniformly (256 bins each) until the boundary bin fits.  Every sweep
-// recomputes the scores with the MFMA (bit-identical), so scores never leave the chip.
+// recomputes the scores with the MFMA (bit-identical), so scores never leave the chip.  Each
+// vector owns one LDS region that holds its histogram or, while it collects, its boundary
+// buffer (a vector is in one state at a time).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,151 +30,196 @@ namespace fadkv {
 
 namespace {
 
-constexpr int VT = 32;          // vectors per workgroup (one MFMA column block)
+constexpr int VT = 32;           // vectors per workgroup (two MFMA column blocks)
 constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
-constexpr int BINS0 = 512;      // first-level bins (1/32 octave), two per 32-bit word
-constexpr int HW = BINS0 / 2 + 1;   // words per vector histogram row, padded against conflicts
-constexpr int RBINS = 256;      // refinement bins (one 32-bit counter per word)
-constexpr int CAP = 128;        // boundary-bin capacity per vector
-constexpr int TPV = THREADS / VT;   // threads per vector in the histogram scans (16)
-constexpr int SHIFT0 = 18;      // key >> 18 = 8 exponent bits + 5 mantissa bits
-constexpr int TOP0 = 492;       // bin holding |score| ~ ||x||; 19 bins (~1.5x) above it
+constexpr int RB = 256;          // bins of every histogram level
+constexpr int CAP = 128;         // boundary-buffer capacity per vector (scores, then atoms)
+constexpr int REGW = RB + 1;     // words per vector region: RB bins + a discard word
+constexpr int DISCARD = RB;
+constexpr int TPV = THREADS / VT;    // threads per vector in the histogram scans (16)
+constexpr int SHIFT0 = 18;       // key >> 18 = 8 exponent bits + 5 mantissa bits
+constexpr int TOP0 = 237;        // level-0 bin of |score| ~ ||x|| is TOP0; 18 bins (~1.5x) above
 
 enum { ST_IDLE = 0, ST_HIST0, ST_COLLECT, ST_REFINE, ST_RCOLLECT };
 enum { PASS_HIST0 = 0, PASS_COLLECT = 1, PASS_GENERIC = 2 };
 
 typedef unsigned long long u64;
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
 template <int DT, int D> struct Geo {
   static constexpr int ROWB = D * Elem<DT>::bytes;   // bytes per row
-  static constexpr int HALFB = ROWB / 2;             // bytes per lane (half a row)
-  static constexpr int U4 = HALFB / 16;              // 16-byte chunks per lane fragment
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int CH = CPR / 4;                 // chunks per lane per row (fragment steps)
+  static constexpr int LOADS = ROWB / 64;            // 1 KB loads per 16-row tile
+  static constexpr int STAGE = 16 * CPR;             // 16-byte slots per wave stage
 };
 
-// 32x32 tile of scores: A = 32 atoms (row = lane % 32), B = 32 vectors (column = lane % 32).
-// Lane half h = lane / 32 supplies elements [h * D/2, (h+1) * D/2) of its row; k-slots are
-// consumed in the same order on A and B, so the sum runs over all D elements.
-template <int DT, int D>
-__device__ __forceinline__ float16_t tile_scores(const uint4 (&a)[Geo<DT, D>::U4],
-                                                 const uint4 (&b)[Geo<DT, D>::U4]) {
-  float16_t acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < Geo<DT, D>::U4; ++i) {
-    if constexpr (DT == DT_F16) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a[i]),
-                                                   __builtin_bit_cast(half8_t, b[i]), acc, 0, 0, 0);
-    } else if constexpr (DT == DT_BF16) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
-                                                    __builtin_bit_cast(bf16x8_t, b[i]), acc, 0, 0, 0);
-    } else {
-      const float *fa = reinterpret_cast<const float *>(&a[i]);
-      const float *fb = reinterpret_cast<const float *>(&b[i]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c], fb[c], acc, 0, 0, 0);
-    }
-  }
-  return acc;
+// stage position of chunk c in row r is c ^ swz(r): 16 rows reading the same chunk hit 16
+// distinct 16-byte bank groups (rows of 256 or 512 bytes: low 4 bits of r; rows of 128
+// bytes: two rows share a 256-byte bank window, so bits 1..3 of r)
+template <int CPR> __device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR >= 16) return r & 15;
+  else return (r >> 1) & (CPR - 1);
 }
 
-// fragment of row `row` (zeros past N): half h of the row, U4 chunks of 16 bytes
+// copy tile t (rows 16 t .. 16 t + 15, clamped to N - 1) into the wave's stage: load j, lane L
+// moves stage slot 64 j + L
 template <int DT, int D>
-__device__ __forceinline__ void load_frag(const uint8_t *base, int row, int N, int h,
-                                          uint4 (&a)[Geo<DT, D>::U4]) {
+__device__ __forceinline__ void issue_tile(const uint8_t *dict_atoms, int N, int t, int lane,
+                                           uint4 *stage) {
   using G = Geo<DT, D>;
-  const bool ok = row < N;
-  const uint4 *src = reinterpret_cast<const uint4 *>(base + (size_t)(ok ? row : 0) * G::ROWB +
-                                                     h * G::HALFB);
 #pragma unroll
-  for (int i = 0; i < G::U4; ++i) a[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < G::LOADS; ++j) {
+    const int slot = 64 * j + lane;
+    const int row = slot / G::CPR;
+    const int chunk = (slot % G::CPR) ^ swz<G::CPR>(row);
+    int grow = t * 16 + row;
+    grow = grow < N ? grow : N - 1;
+    __builtin_amdgcn_global_load_lds((gbl_void *)(dict_atoms + (size_t)grow * G::ROWB + chunk * 16),
+                                     (lds_void *)(stage + 64 * j), 16, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(0) / lgkmcnt(0) (gfx9 encoding; the other counters left at their maximum)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// 16x16 scores of one tile for both vector blocks
+template <int DT, int D>
+__device__ __forceinline__ void tile_scores(const uint4 (&a)[Geo<DT, D>::CH],
+                                            const uint4 (&b)[2][Geo<DT, D>::CH], float4_t &acc0,
+                                            float4_t &acc1) {
+  acc0 = float4_t{0.f, 0.f, 0.f, 0.f};
+  acc1 = acc0;
+#pragma unroll
+  for (int i = 0; i < Geo<DT, D>::CH; ++i) {
+    if constexpr (DT == DT_F16) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a[i]),
+                                                    __builtin_bit_cast(half8_t, b[0][i]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a[i]),
+                                                    __builtin_bit_cast(half8_t, b[1][i]), acc1, 0, 0, 0);
+    } else if constexpr (DT == DT_BF16) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                     __builtin_bit_cast(bf16x8_t, b[0][i]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                     __builtin_bit_cast(bf16x8_t, b[1][i]), acc1, 0, 0, 0);
+    } else {
+      // fp32: one k element per lane and instruction; element e of the chunk at step e
+      const uint32_t av[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+      const uint32_t b0[4] = {b[0][i].x, b[0][i].y, b[0][i].z, b[0][i].w};
+      const uint32_t b1[4] = {b[1][i].x, b[1][i].y, b[1][i].z, b[1][i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[e]), __uint_as_float(b0[e]), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[e]), __uint_as_float(b1[e]), acc1, 0, 0, 0);
+      }
+    }
+  }
 }
 
 __device__ __forceinline__ u64 comp_key(uint32_t key31, int atom) {
   return ((u64)key31 << 16) | (u64)(0xFFFFu - (uint32_t)atom);
 }
 
-struct LaneState {          // the state of the lane's vector during one sweep
+struct VecState {           // one of the lane's two vectors during one sweep
   bool active;
   int state;
-  int base;                 // level-0 bin offset
+  int vi;                   // vector within the workgroup
+  int base;                 // level-0: key >> 18 of bin 0
+  int off;                  // level-0: region word of (key >> 18) is (key >> 18) + off
   uint32_t lo32, hi32;      // boundary bin in 31-bit key space (level 0)
   u64 lo, hi;               // boundary range in composite-key space (refinement)
   int shift;
+  uint16_t *pidx;
+  float *psig;
 };
 
 struct Shared {
-  uint32_t *hist;
-  float *bsig;
-  int *bidx;
+  uint32_t *reg;            // VT regions of REGW words
   int *above;
   int *bcnt;
 };
 
-// one sweep over the dictionary; PASS selects what every score of an active lane does
-template <int DT, int D, int PASS>
-__device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, int wave, int col,
-                                      int h, const uint4 (&b)[Geo<DT, D>::U4], const LaneState &ls,
-                                      const Shared &sh, uint16_t *pidx, float *psig) {
-  using G = Geo<DT, D>;
-  const int ntiles = (N + 31) / 32;
-  uint4 a[G::U4], an[G::U4];
-  if (wave < ntiles) load_frag<DT, D>(dict_atoms, wave * 32 + col, N, h, a);
-  for (int t = wave; t < ntiles; t += WAVES) {
-    const bool more = t + WAVES < ntiles;
-    if (more) load_frag<DT, D>(dict_atoms, (t + WAVES) * 32 + col, N, h, an);
-    const float16_t acc = tile_scores<DT, D>(a, b);
-    if (ls.active) {
-      const bool full = t * 32 + 32 <= N;
+template <int PASS, bool CHECK>
+__device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, int n,
+                                        const VecState &vs, const Shared &sh) {
+  uint32_t *reg = sh.reg + vs.vi * REGW;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int atom = t * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (!full && atom >= N) continue;
-        const float sc = acc[r];
-        const uint32_t key = __float_as_uint(sc) & 0x7fffffffu;
-        if constexpr (PASS == PASS_HIST0) {
-          int bin = (int)(key >> SHIFT0) - ls.base;
-          bin = bin < 0 ? 0 : (bin > BINS0 - 1 ? BINS0 - 1 : bin);
-          atomicAdd(&sh.hist[col * HW + (bin >> 1)], 1u << ((bin & 1) << 4));
-        } else if constexpr (PASS == PASS_COLLECT) {
-          if (key >= ls.hi32) {
-            const int pos = atomicAdd(&sh.above[col], 1);
-            if (pos < n) {
-              pidx[pos] = (uint16_t)atom;
-              psig[pos] = sc;
-            }
-          } else if (key >= ls.lo32) {
-            const int pos = atomicAdd(&sh.bcnt[col], 1);
-            if (pos < CAP) {
-              sh.bsig[col * CAP + pos] = sc;
-              sh.bidx[col * CAP + pos] = atom;
-            }
-          }
-        } else {
-          const u64 K = comp_key(key, atom);
-          if (ls.state == ST_REFINE) {
-            if (K >= ls.lo && K < ls.hi)
-              atomicAdd(&sh.hist[col * HW + (int)((K - ls.lo) >> ls.shift)], 1u);
-          } else if (K >= ls.hi) {
-            const int pos = atomicAdd(&sh.above[col], 1);
-            if (pos < n) {
-              pidx[pos] = (uint16_t)atom;
-              psig[pos] = sc;
-            }
-          } else if (K >= ls.lo) {
-            const int pos = atomicAdd(&sh.bcnt[col], 1);
-            if (pos < CAP) {
-              sh.bsig[col * CAP + pos] = sc;
-              sh.bidx[col * CAP + pos] = atom;
-            }
-          }
+  for (int e = 0; e < 4; ++e) {
+    const int atom = atom0 + e;
+    const float sc = acc[e];
+    const uint32_t key = __float_as_uint(sc) & 0x7fffffffu;
+    if constexpr (PASS == PASS_HIST0) {
+      const int k18 = (int)(key >> SHIFT0);
+      const int kc = k18 < vs.base ? vs.base : (k18 > vs.base + RB - 1 ? vs.base + RB - 1 : k18);
+      int w = kc + vs.off;
+      if (CHECK && atom >= N) w = vs.vi * REGW + DISCARD;
+      atomicAdd(&sh.reg[w], 1u);
+    } else if constexpr (PASS == PASS_COLLECT) {
+      if (CHECK && atom >= N) continue;
+      if (key >= vs.hi32) {
+        const int pos = atomicAdd(&sh.above[vs.vi], 1);
+        if (pos < n) {
+          vs.pidx[pos] = (uint16_t)atom;
+          vs.psig[pos] = sc;
+        }
+      } else if (key >= vs.lo32) {
+        const int pos = atomicAdd(&sh.bcnt[vs.vi], 1);
+        if (pos < CAP) {
+          reg[pos] = __float_as_uint(sc);
+          reg[CAP + pos] = (uint32_t)atom;
+        }
+      }
+    } else {
+      if (CHECK && atom >= N) continue;
+      const u64 K = comp_key(key, atom);
+      if (vs.state == ST_REFINE) {
+        if (K >= vs.lo && K < vs.hi) atomicAdd(&reg[(int)((K - vs.lo) >> vs.shift)], 1u);
+      } else if (K >= vs.hi) {
+        const int pos = atomicAdd(&sh.above[vs.vi], 1);
+        if (pos < n) {
+          vs.pidx[pos] = (uint16_t)atom;
+          vs.psig[pos] = sc;
+        }
+      } else if (K >= vs.lo) {
+        const int pos = atomicAdd(&sh.bcnt[vs.vi], 1);
+        if (pos < CAP) {
+          reg[pos] = __float_as_uint(sc);
+          reg[CAP + pos] = (uint32_t)atom;
         }
       }
     }
-    if (more) {
+  }
+}
+
+// one sweep over the dictionary; PASS selects what every score of an active vector does
+template <int DT, int D, int PASS>
+__device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, int wave, int lane,
+                                      const uint4 (&b)[2][Geo<DT, D>::CH], const VecState (&vs)[2],
+                                      const Shared &sh, uint4 *stage) {
+  using G = Geo<DT, D>;
+  const int ntiles = (N + 15) / 16;
+  const int r = lane % 16, g = lane / 16;
+  if (wave < ntiles) issue_tile<DT, D>(dict_atoms, N, wave, lane, stage);
+  for (int t = wave; t < ntiles; t += WAVES) {
+    wait_vmem();   // the tile is in the stage
+    uint4 a[G::CH];
 #pragma unroll
-      for (int i = 0; i < G::U4; ++i) a[i] = an[i];
+    for (int i = 0; i < G::CH; ++i) a[i] = stage[r * G::CPR + ((4 * i + g) ^ swz<G::CPR>(r))];
+    wait_lds();    // fragments in registers: the stage may be overwritten
+    if (t + WAVES < ntiles) issue_tile<DT, D>(dict_atoms, N, t + WAVES, lane, stage);
+    float4_t acc0, acc1;
+    tile_scores<DT, D>(a, b, acc0, acc1);
+    const int atom0 = t * 16 + 4 * g;
+    if (t * 16 + 16 <= N) {
+      if (vs[0].active) process<PASS, false>(acc0, atom0, N, n, vs[0], sh);
+      if (vs[1].active) process<PASS, false>(acc1, atom0, N, n, vs[1], sh);
+    } else {
+      if (vs[0].active) process<PASS, true>(acc0, atom0, N, n, vs[0], sh);
+      if (vs[1].active) process<PASS, true>(acc1, atom0, N, n, vs[1], sh);
     }
   }
 }
@@ -177,14 +227,13 @@ __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, i
 }  // namespace
 
 template <int DT, int D>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void score_topn_kernel(
+__global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void score_topn_kernel(
     const uint8_t *__restrict__ atoms, const uint8_t *__restrict__ X, int num_dicts, int N, int M,
     int n, uint16_t *__restrict__ pool_idx, float *__restrict__ pool_sig,
     uint8_t *__restrict__ vstat) {
   using G = Geo<DT, D>;
-  __shared__ uint32_t hist[VT * HW];
-  __shared__ float bsig[VT * CAP];
-  __shared__ int bidx[VT * CAP];
+  __shared__ __attribute__((aligned(16))) uint4 s_stage[WAVES * G::STAGE];
+  __shared__ uint32_t s_reg[VT * REGW];
   __shared__ u64 s_lo[VT], s_hi[VT];
   __shared__ uint32_t s_lo32[VT], s_hi32[VT];
   __shared__ int s_state[VT], s_need[VT], s_base[VT], s_shift[VT], s_above[VT], s_bcnt[VT];
@@ -197,21 +246,33 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (dict >= num_dicts) return;
   const int v0 = (rr % nvb) * VT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, h = lane >> 5;
   const uint8_t *dict_atoms = atoms + (size_t)dict * N * G::ROWB;
   const size_t vbase = (size_t)dict * M + v0;
-  const Shared sh{hist, bsig, bidx, s_above, s_bcnt};
+  const Shared sh{s_reg, s_above, s_bcnt};
+  uint4 *stage = s_stage + wave * G::STAGE;
 
   if (tid < VT) {
     int state = ST_IDLE;
     if (v0 + tid < M) {
-      const uint8_t *xr = X + (vbase + tid) * G::ROWB;
+      const uint4 *xr = reinterpret_cast<const uint4 *>(X + (vbase + tid) * G::ROWB);
       float ss = 0.f;
       bool fin = true;
-      for (int i = 0; i < D; ++i) {
-        const float f = elem_f<DT>(xr, i);
-        fin = fin && __builtin_isfinite(f);
-        ss += f * f;
+      for (int c = 0; c < G::CPR; ++c) {
+        const uint4 q = xr[c];
+        const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if constexpr (DT == DT_F32) {
+            const float f = __uint_as_float(w4[u]);
+            fin = fin && __builtin_isfinite(f);
+            ss = fmaf(f, f, ss);
+          } else {
+            const float f0 = lo_f<DT>(w4[u]), f1 = hi_f<DT>(w4[u]);
+            fin = fin && __builtin_isfinite(f0) && __builtin_isfinite(f1);
+            ss = fmaf(f0, f0, ss);
+            ss = fmaf(f1, f1, ss);
+          }
+        }
       }
       const uint8_t st = !fin ? VS_NONFINITE : (ss == 0.f ? VS_ZERO : VS_NORMAL);
       vstat[vbase + tid] = st;
@@ -225,40 +286,47 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     s_above[tid] = 0;
     s_bcnt[tid] = 0;
   }
-  uint4 b[G::U4];
-  {
-    const bool ok = v0 + col < M;
-    const uint4 *src = reinterpret_cast<const uint4 *>(X + (vbase + (ok ? col : 0)) * G::ROWB +
-                                                       h * G::HALFB);
+  // B fragments: block k, step i holds chunk 4 i + lane / 16 of vector 16 k + lane % 16
+  uint4 b[2][G::CH];
 #pragma unroll
-    for (int i = 0; i < G::U4; ++i) b[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
+  for (int k = 0; k < 2; ++k) {
+    const int v = 16 * k + lane % 16;
+    const bool ok = v0 + v < M;
+    const uint4 *src = reinterpret_cast<const uint4 *>(X + (vbase + (ok ? v : 0)) * G::ROWB);
+#pragma unroll
+    for (int i = 0; i < G::CH; ++i) b[k][i] = ok ? src[4 * i + lane / 16] : make_uint4(0, 0, 0, 0);
   }
-  for (int i = tid; i < VT * HW; i += THREADS) hist[i] = 0u;
+  for (int i = tid; i < VT * REGW; i += THREADS) s_reg[i] = 0u;
   __syncthreads();
 
-  uint16_t *pidx = pool_idx + (vbase + col) * (size_t)n;
-  float *psig = pool_sig + (vbase + col) * (size_t)n;
+  VecState vs[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    vs[k] = VecState{};
+    vs[k].vi = 16 * k + lane % 16;
+    vs[k].pidx = pool_idx + (vbase + vs[k].vi) * (size_t)n;
+    vs[k].psig = pool_sig + (vbase + vs[k].vi) * (size_t)n;
+  }
 
   // ---- sweep 1: level-0 histogram -----------------------------------------------------------
-  {
-    LaneState ls{};
-    ls.active = s_state[col] == ST_HIST0;
-    ls.base = s_base[col];
-    sweep<DT, D, PASS_HIST0>(dict_atoms, N, n, wave, col, h, b, ls, sh, pidx, psig);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    vs[k].active = s_state[vs[k].vi] == ST_HIST0;
+    vs[k].base = s_base[vs[k].vi];
+    vs[k].off = vs[k].vi * REGW - vs[k].base;
   }
+  sweep<DT, D, PASS_HIST0>(dict_atoms, N, n, wave, lane, b, vs, sh, stage);
   __syncthreads();
   {
-    // TPV threads per vector: thread `sub` covers bins [32 sub, 32 sub + 32); a suffix sum
-    // of the per-thread counts locates the bin holding the n-th largest key
+    // TPV threads per vector: thread `sub` covers bins [16 sub, 16 sub + 16); a suffix sum of
+    // the per-thread counts locates the bin holding the n-th largest key
     const int v = tid / TPV, sub = tid % TPV;
     const bool on = s_state[v] == ST_HIST0;
+    constexpr int BPT = RB / TPV;
     uint32_t part = 0;
     if (on) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const uint32_t w = hist[v * HW + 16 * sub + q];
-        part += (w & 0xffffu) + (w >> 16);
-      }
+      for (int q = 0; q < BPT; ++q) part += s_reg[v * REGW + BPT * sub + q];
     }
     uint32_t suf = part;
 #pragma unroll
@@ -269,9 +337,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     const uint32_t need = (uint32_t)n;
     if (on && suf - part < need && suf >= need) {
       uint32_t above = suf - part, cnt = 0;
-      int bstar = 32 * sub;
-      for (int bin = 32 * sub + 31; bin >= 32 * sub; --bin) {
-        const uint32_t c = (hist[v * HW + (bin >> 1)] >> ((bin & 1) << 4)) & 0xffffu;
+      int bstar = BPT * sub;
+      for (int bin = BPT * sub + BPT - 1; bin >= BPT * sub; --bin) {
+        const uint32_t c = s_reg[v * REGW + bin];
         if (above + c >= need) {
           bstar = bin;
           cnt = c;
@@ -281,7 +349,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
       }
       const long long bs = (long long)s_base[v] + bstar;
       long long lob = bstar == 0 ? 0 : bs << SHIFT0;
-      long long hib = bstar == BINS0 - 1 ? (1ll << 31) : (bs + 1) << SHIFT0;
+      long long hib = bstar == RB - 1 ? (1ll << 31) : (bs + 1) << SHIFT0;
       lob = lob < 0 ? 0 : (lob > (1ll << 31) ? (1ll << 31) : lob);
       hib = hib < 0 ? 0 : (hib > (1ll << 31) ? (1ll << 31) : hib);
       s_need[v] = (int)(need - above);
@@ -302,46 +370,45 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
   __syncthreads();
 
   // ---- sweep 2: collect for every vector whose boundary bin fits -----------------------------
-  {
-    LaneState ls{};
-    ls.active = s_state[col] == ST_COLLECT;
-    ls.lo32 = s_lo32[col];
-    ls.hi32 = s_hi32[col];
-    sweep<DT, D, PASS_COLLECT>(dict_atoms, N, n, wave, col, h, b, ls, sh, pidx, psig);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    vs[k].active = s_state[vs[k].vi] == ST_COLLECT;
+    vs[k].lo32 = s_lo32[vs[k].vi];
+    vs[k].hi32 = s_hi32[vs[k].vi];
   }
+  sweep<DT, D, PASS_COLLECT>(dict_atoms, N, n, wave, lane, b, vs, sh, stage);
   __syncthreads();
 
   // ---- resolve boundaries; refine the rest (rare) -------------------------------------------
   for (int pass = 0;; ++pass) {
-    // vectors that collected this pass: take the `need` largest keys of the boundary bin
+    // vectors that collected this pass: take the `need` largest keys of the boundary buffer
     for (int slot = tid; slot < VT * CAP; slot += THREADS) {
       const int v = slot / CAP, e = slot % CAP;
       const int st = s_state[v];
       const int cnt = s_bcnt[v] < CAP ? s_bcnt[v] : CAP;
       if ((st != ST_COLLECT && st != ST_RCOLLECT) || e >= cnt) continue;
-      const u64 Ke = comp_key(__float_as_uint(bsig[v * CAP + e]) & 0x7fffffffu, bidx[v * CAP + e]);
+      const uint32_t *reg = s_reg + v * REGW;
+      const u64 Ke = comp_key(reg[e] & 0x7fffffffu, (int)reg[CAP + e]);
       int rank = 0;
-      for (int q = 0; q < cnt; ++q) {
-        const u64 Kq = comp_key(__float_as_uint(bsig[v * CAP + q]) & 0x7fffffffu, bidx[v * CAP + q]);
-        rank += Kq > Ke;
-      }
+      for (int q = 0; q < cnt; ++q) rank += comp_key(reg[q] & 0x7fffffffu, (int)reg[CAP + q]) > Ke;
       const int need = s_need[v];
       if (rank < need && need <= n) {
         const size_t row = (vbase + v) * (size_t)n;
         const int pos = n - need + rank;
-        pool_idx[row + pos] = (uint16_t)bidx[v * CAP + e];
-        pool_sig[row + pos] = bsig[v * CAP + e];
+        pool_idx[row + pos] = (uint16_t)reg[CAP + e];
+        pool_sig[row + pos] = __uint_as_float(reg[e]);
       }
     }
     __syncthreads();
     {
-      // refinement finalize: TPV threads per vector over RBINS bins
+      // refinement finalize: TPV threads per vector over RB bins
       const int v = tid / TPV, sub = tid % TPV;
       const int st = s_state[v];
+      constexpr int BPT = RB / TPV;
       uint32_t part = 0;
       if (st == ST_REFINE && pass > 0) {
 #pragma unroll
-        for (int q = 0; q < RBINS / TPV; ++q) part += hist[v * HW + (RBINS / TPV) * sub + q];
+        for (int q = 0; q < BPT; ++q) part += s_reg[v * REGW + BPT * sub + q];
       }
       uint32_t suf = part;
 #pragma unroll
@@ -353,9 +420,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
       const uint32_t need = (uint32_t)s_need[v];
       if (st == ST_REFINE && pass > 0 && suf - part < need && suf >= need) {
         uint32_t above = suf - part, cnt = 0;
-        int bstar = (RBINS / TPV) * sub;
-        for (int bin = (RBINS / TPV) * sub + RBINS / TPV - 1; bin >= (RBINS / TPV) * sub; --bin) {
-          const uint32_t c = hist[v * HW + bin];
+        int bstar = BPT * sub;
+        for (int bin = BPT * sub + BPT - 1; bin >= BPT * sub; --bin) {
+          const uint32_t c = s_reg[v * REGW + bin];
           if (above + c >= need) {
             bstar = bin;
             cnt = c;
@@ -385,22 +452,23 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
       // most 7 refinement sweeps and one collect sweep; the bound only guards the loop
       s_busy = busy && pass < 10;
     }
-    for (int i = tid; i < VT * HW; i += THREADS) hist[i] = 0u;
+    for (int i = tid; i < VT * REGW; i += THREADS) s_reg[i] = 0u;
     if (tid < VT) {
       s_above[tid] = s_state[tid] == ST_RCOLLECT ? 0 : s_above[tid];
       s_bcnt[tid] = 0;
     }
     __syncthreads();
     if (!s_busy) break;
-    {
-      LaneState ls{};
-      ls.state = s_state[col];
-      ls.active = ls.state == ST_REFINE || ls.state == ST_RCOLLECT;
-      ls.lo = s_lo[col];
-      ls.hi = s_hi[col];
-      ls.shift = s_shift[col];
-      sweep<DT, D, PASS_GENERIC>(dict_atoms, N, n, wave, col, h, b, ls, sh, pidx, psig);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int v = vs[k].vi;
+      vs[k].state = s_state[v];
+      vs[k].active = vs[k].state == ST_REFINE || vs[k].state == ST_RCOLLECT;
+      vs[k].lo = s_lo[v];
+      vs[k].hi = s_hi[v];
+      vs[k].shift = s_shift[v];
     }
+    sweep<DT, D, PASS_GENERIC>(dict_atoms, N, n, wave, lane, b, vs, sh, stage);
     __syncthreads();
   }
 }
