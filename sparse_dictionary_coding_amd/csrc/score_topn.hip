@@ -46,8 +46,6 @@ enum { PASS_HIST0 = 0, PASS_COLLECT = 1, PASS_GENERIC = 2 };
 
 typedef unsigned long long u64;
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 template <int DT, int D> struct Geo {
   static constexpr int ROWB = D * Elem<DT>::bytes;   // bytes per row
@@ -65,11 +63,29 @@ template <int CPR> __device__ __forceinline__ int swz(int r) {
   else return (r >> 1) & (CPR - 1);
 }
 
+// 16 bytes per lane global -> LDS (lane L writes LDS bytes [lds + 16 L, lds + 16 L + 16)).
+// Written as assembly so that the compiler does not treat the copy as an LDS store that
+// every later LDS access must wait for: the sweep orders the stage by hand (wait_vmem before
+// the fragment reads, wait_lds before the stage is refilled), and the histogram and boundary
+// regions never overlap the stages.  M0 holds the LDS address; one wait state after writing it.
+// M0 is otherwise unused by these kernels (no LDS DMA builtins, no indexed register moves),
+// so clobbering it cannot break a value the compiler keeps there; a CPU test checks the
+// generated code for any other M0 use.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // copy tile t (rows 16 t .. 16 t + 15, clamped to N - 1) into the wave's stage: load j, lane L
 // moves stage slot 64 j + L
 template <int DT, int D>
 __device__ __forceinline__ void issue_tile(const uint8_t *dict_atoms, int N, int t, int lane,
-                                           uint4 *stage) {
+                                           uint32_t stage_lds) {
   using G = Geo<DT, D>;
 #pragma unroll
   for (int j = 0; j < G::LOADS; ++j) {
@@ -78,8 +94,7 @@ __device__ __forceinline__ void issue_tile(const uint8_t *dict_atoms, int N, int
     const int chunk = (slot % G::CPR) ^ swz<G::CPR>(row);
     int grow = t * 16 + row;
     grow = grow < N ? grow : N - 1;
-    __builtin_amdgcn_global_load_lds((gbl_void *)(dict_atoms + (size_t)grow * G::ROWB + chunk * 16),
-                                     (lds_void *)(stage + 64 * j), 16, 0, 0);
+    copy16_to_lds(dict_atoms + (size_t)grow * G::ROWB + chunk * 16, stage_lds + 1024u * j);
   }
 }
 
@@ -153,8 +168,7 @@ __device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, i
     const float sc = acc[e];
     const uint32_t key = __float_as_uint(sc) & 0x7fffffffu;
     if constexpr (PASS == PASS_HIST0) {
-      const int k18 = (int)(key >> SHIFT0);
-      const int kc = k18 < vs.base ? vs.base : (k18 > vs.base + RB - 1 ? vs.base + RB - 1 : k18);
+      const int kc = min(max((int)(key >> SHIFT0), vs.base), vs.base + RB - 1);
       int w = kc + vs.off;
       if (CHECK && atom >= N) w = vs.vi * REGW + DISCARD;
       atomicAdd(&sh.reg[w], 1u);
@@ -199,18 +213,18 @@ __device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, i
 template <int DT, int D, int PASS>
 __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, int wave, int lane,
                                       const uint4 (&b)[2][Geo<DT, D>::CH], const VecState (&vs)[2],
-                                      const Shared &sh, uint4 *stage) {
+                                      const Shared &sh, const uint4 *stage, uint32_t stage_lds) {
   using G = Geo<DT, D>;
   const int ntiles = (N + 15) / 16;
   const int r = lane % 16, g = lane / 16;
-  if (wave < ntiles) issue_tile<DT, D>(dict_atoms, N, wave, lane, stage);
+  if (wave < ntiles) issue_tile<DT, D>(dict_atoms, N, wave, lane, stage_lds);
   for (int t = wave; t < ntiles; t += WAVES) {
     wait_vmem();   // the tile is in the stage
     uint4 a[G::CH];
 #pragma unroll
     for (int i = 0; i < G::CH; ++i) a[i] = stage[r * G::CPR + ((4 * i + g) ^ swz<G::CPR>(r))];
     wait_lds();    // fragments in registers: the stage may be overwritten
-    if (t + WAVES < ntiles) issue_tile<DT, D>(dict_atoms, N, t + WAVES, lane, stage);
+    if (t + WAVES < ntiles) issue_tile<DT, D>(dict_atoms, N, t + WAVES, lane, stage_lds);
     float4_t acc0, acc1;
     tile_scores<DT, D>(a, b, acc0, acc1);
     const int atom0 = t * 16 + 4 * g;
@@ -250,6 +264,9 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
   const size_t vbase = (size_t)dict * M + v0;
   const Shared sh{s_reg, s_above, s_bcnt};
   uint4 *stage = s_stage + wave * G::STAGE;
+  // LDS byte address of the stage (wave-uniform, for M0)
+  const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)stage);
 
   if (tid < VT) {
     int state = ST_IDLE;
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
     vs[k].base = s_base[vs[k].vi];
     vs[k].off = vs[k].vi * REGW - vs[k].base;
   }
-  sweep<DT, D, PASS_HIST0>(dict_atoms, N, n, wave, lane, b, vs, sh, stage);
+  sweep<DT, D, PASS_HIST0>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
   __syncthreads();
   {
     // TPV threads per vector: thread `sub` covers bins [16 sub, 16 sub + 16); a suffix sum of
@@ -376,7 +393,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
     vs[k].lo32 = s_lo32[vs[k].vi];
     vs[k].hi32 = s_hi32[vs[k].vi];
   }
-  sweep<DT, D, PASS_COLLECT>(dict_atoms, N, n, wave, lane, b, vs, sh, stage);
+  sweep<DT, D, PASS_COLLECT>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
   __syncthreads();
 
   // ---- resolve boundaries; refine the rest (rare) -------------------------------------------
@@ -468,7 +485,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
       vs[k].hi = s_hi[v];
       vs[k].shift = s_shift[v];
     }
-    sweep<DT, D, PASS_GENERIC>(dict_atoms, N, n, wave, lane, b, vs, sh, stage);
+    sweep<DT, D, PASS_GENERIC>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
     __syncthreads();
   }
 }

@@ -1,0 +1,36 @@
+"""Checks on the generated gfx950 code that the kernels' correctness relies on (CPU only).
+
+The screening kernel writes M0 in inline assembly to drive its global -> LDS copies; that is
+only sound while the compiler itself keeps nothing in M0 in these kernels.  The test compiles
+the source to assembly and requires every M0 access to be one of those copies.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from sparse_dictionary_coding_amd import build
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_m0_written_only_by_lds_copies(tmp_path):
+    src = os.path.join(build.CSRC, "score_topn.hip")
+    out = tmp_path / "score_topn.s"
+    cmd = [HIPCC, *build.HIPCC_FLAGS, f"-I{build.INCLUDE}", f"-I{build.CSRC}",
+           "--cuda-device-only", "-S", src, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = [ln.strip() for ln in out.read_text().splitlines()]
+    copies = 0
+    for i, ln in enumerate(lines):
+        if ln.startswith(";") or not re.search(r"\bm0\b", ln):
+            continue
+        assert re.fullmatch(r"s_mov_b32 m0, s\d+", ln), f"unexpected M0 use: {ln}"
+        assert lines[i + 1] == "s_nop 0", lines[i + 1]
+        assert lines[i + 2].startswith("global_load_lds_dwordx4 "), lines[i + 2]
+        copies += 1
+    assert copies > 0
