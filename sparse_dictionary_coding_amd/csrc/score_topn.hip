@@ -73,28 +73,64 @@ template <int CPR> __device__ __forceinline__ int swz(int r) {
 // generated code for any other M0 use.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// per-lane 64-bit address
 __device__ __forceinline__ void copy16_to_lds(const void *gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
+// wave-uniform 64-bit base + per-lane 32-bit offset
+__device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// copy tile t (rows 16 t .. 16 t + 15, clamped to N - 1) into the wave's stage: load j, lane L
-// moves stage slot 64 j + L
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
+
+// Tile t is rows 16 t .. 16 t + 15; load j, lane L moves stage slot 64 j + L, which holds
+// row (64 j + L) / CPR, chunk ((64 j + L) % CPR) ^ swz(row).  tile_offsets gives the lane's
+// byte offsets inside a tile; a tile that ends past N takes the clamped path (rows >= N read
+// row N - 1, whose scores are discarded).
 template <int DT, int D>
-__device__ __forceinline__ void issue_tile(const uint8_t *dict_atoms, int N, int t, int lane,
-                                           uint32_t stage_lds) {
+__device__ __forceinline__ void tile_offsets(int lane, uint32_t (&off)[Geo<DT, D>::LOADS]) {
   using G = Geo<DT, D>;
 #pragma unroll
   for (int j = 0; j < G::LOADS; ++j) {
     const int slot = 64 * j + lane;
     const int row = slot / G::CPR;
     const int chunk = (slot % G::CPR) ^ swz<G::CPR>(row);
-    int grow = t * 16 + row;
-    grow = grow < N ? grow : N - 1;
-    copy16_to_lds(dict_atoms + (size_t)grow * G::ROWB + chunk * 16, stage_lds + 1024u * j);
+    off[j] = (uint32_t)(row * G::ROWB + chunk * 16);
+  }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void issue_tile(const uint8_t *dict_atoms, int N, int t, int lane,
+                                           const uint32_t (&off)[Geo<DT, D>::LOADS],
+                                           uint32_t stage_lds) {
+  using G = Geo<DT, D>;
+  if (t * 16 + 16 <= N) {
+    const uint8_t *tile = uniform_ptr(dict_atoms + (size_t)t * 16 * G::ROWB);
+#pragma unroll
+    for (int j = 0; j < G::LOADS; ++j) copy16_to_lds(tile, off[j], stage_lds + 1024u * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < G::LOADS; ++j) {
+      const int slot = 64 * j + lane;
+      const int row = slot / G::CPR;
+      const int chunk = (slot % G::CPR) ^ swz<G::CPR>(row);
+      int grow = t * 16 + row;
+      grow = grow < N ? grow : N - 1;
+      copy16_to_lds(dict_atoms + (size_t)grow * G::ROWB + chunk * 16, stage_lds + 1024u * j);
+    }
   }
 }
 
@@ -172,21 +208,6 @@ __device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, i
       int w = kc + vs.off;
       if (CHECK && atom >= N) w = vs.vi * REGW + DISCARD;
       atomicAdd(&sh.reg[w], 1u);
-    } else if constexpr (PASS == PASS_COLLECT) {
-      if (CHECK && atom >= N) continue;
-      if (key >= vs.hi32) {
-        const int pos = atomicAdd(&sh.above[vs.vi], 1);
-        if (pos < n) {
-          vs.pidx[pos] = (uint16_t)atom;
-          vs.psig[pos] = sc;
-        }
-      } else if (key >= vs.lo32) {
-        const int pos = atomicAdd(&sh.bcnt[vs.vi], 1);
-        if (pos < CAP) {
-          reg[pos] = __float_as_uint(sc);
-          reg[CAP + pos] = (uint32_t)atom;
-        }
-      }
     } else {
       if (CHECK && atom >= N) continue;
       const u64 K = comp_key(key, atom);
@@ -209,26 +230,84 @@ __device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, i
   }
 }
 
-// one sweep over the dictionary; PASS selects what every score of an active vector does
-template <int DT, int D, int PASS>
+// Collect pass over one tile for both vectors.  Hits (|score| at or above the boundary bin)
+// are rare, so each lane first gathers its eight hit flags into a mask and the wave then loops
+// over the hits, one per lane and round (rounds = the largest hit count of a lane, not eight).
+template <bool CHECK>
+__device__ __forceinline__ void collect_tile(const float4_t &acc0, const float4_t &acc1, int atom0,
+                                             int N, int n, const VecState (&vs)[2],
+                                             const Shared &sh) {
+  const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+  uint32_t m = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const VecState &q = vs[b >> 2];
+    const uint32_t key = __float_as_uint(v[b]) & 0x7fffffffu;
+    const bool ok = q.active && (!CHECK || atom0 + (b & 3) < N);
+    m |= (ok && key >= q.lo32) ? 1u << b : 0u;
+  }
+  while (__builtin_amdgcn_ballot_w64(m != 0)) {
+    if (m) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1;
+      // v[b] by a select tree on the bits of b (no indexed register access)
+      const bool b0 = b & 1, b1 = b & 2, b2 = b & 4;
+      const float c0 = b1 ? (b0 ? v[3] : v[2]) : (b0 ? v[1] : v[0]);
+      const float c1 = b1 ? (b0 ? v[7] : v[6]) : (b0 ? v[5] : v[4]);
+      const float sc = b2 ? c1 : c0;
+      const int vi = b2 ? vs[1].vi : vs[0].vi;
+      const uint32_t hi32 = b2 ? vs[1].hi32 : vs[0].hi32;
+      const int atom = atom0 + (b & 3);
+      const bool hi = (__float_as_uint(sc) & 0x7fffffffu) >= hi32;
+      const int pos = atomicAdd(hi ? &sh.above[vi] : &sh.bcnt[vi], 1);
+      if (hi) {
+        if (pos < n) {
+          uint16_t *pidx = b2 ? vs[1].pidx : vs[0].pidx;
+          float *psig = b2 ? vs[1].psig : vs[0].psig;
+          pidx[pos] = (uint16_t)atom;
+          psig[pos] = sc;
+        }
+      } else if (pos < CAP) {
+        uint32_t *reg = sh.reg + vi * REGW;
+        reg[pos] = __float_as_uint(sc);
+        reg[CAP + pos] = (uint32_t)atom;
+      }
+    }
+  }
+}
+
+// One sweep over the dictionary; PASS selects what every score of an active vector does.
+// Wave w takes tiles w, w + 8, ...; REV runs them from the last one down, so that a sweep
+// that follows another starts on the tiles the previous one left in L2.
+template <int DT, int D, int PASS, bool REV = false>
 __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, int wave, int lane,
                                       const uint4 (&b)[2][Geo<DT, D>::CH], const VecState (&vs)[2],
                                       const Shared &sh, const uint4 *stage, uint32_t stage_lds) {
   using G = Geo<DT, D>;
   const int ntiles = (N + 15) / 16;
   const int r = lane % 16, g = lane / 16;
-  if (wave < ntiles) issue_tile<DT, D>(dict_atoms, N, wave, lane, stage_lds);
-  for (int t = wave; t < ntiles; t += WAVES) {
+  uint32_t off[G::LOADS];
+  tile_offsets<DT, D>(lane, off);
+  if (wave >= ntiles) return;
+  const int tlast = wave + (ntiles - 1 - wave) / WAVES * WAVES;
+  const int tfirst = REV ? tlast : wave, step = REV ? -WAVES : WAVES;
+  issue_tile<DT, D>(dict_atoms, N, tfirst, lane, off, stage_lds);
+  for (int t = tfirst; REV ? t >= 0 : t < ntiles; t += step) {
     wait_vmem();   // the tile is in the stage
     uint4 a[G::CH];
 #pragma unroll
     for (int i = 0; i < G::CH; ++i) a[i] = stage[r * G::CPR + ((4 * i + g) ^ swz<G::CPR>(r))];
     wait_lds();    // fragments in registers: the stage may be overwritten
-    if (t + WAVES < ntiles) issue_tile<DT, D>(dict_atoms, N, t + WAVES, lane, stage_lds);
+    if (REV ? t - WAVES >= 0 : t + WAVES < ntiles)
+      issue_tile<DT, D>(dict_atoms, N, t + step, lane, off, stage_lds);
     float4_t acc0, acc1;
     tile_scores<DT, D>(a, b, acc0, acc1);
     const int atom0 = t * 16 + 4 * g;
-    if (t * 16 + 16 <= N) {
+    const bool full = t * 16 + 16 <= N;
+    if constexpr (PASS == PASS_COLLECT) {
+      if (full) collect_tile<false>(acc0, acc1, atom0, N, n, vs, sh);
+      else collect_tile<true>(acc0, acc1, atom0, N, n, vs, sh);
+    } else if (full) {
       if (vs[0].active) process<PASS, false>(acc0, atom0, N, n, vs[0], sh);
       if (vs[1].active) process<PASS, false>(acc1, atom0, N, n, vs[1], sh);
     } else {
@@ -259,7 +338,8 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
   const int dict = xcd + 8 * (rr / nvb);
   if (dict >= num_dicts) return;
   const int v0 = (rr % nvb) * VT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint8_t *dict_atoms = atoms + (size_t)dict * N * G::ROWB;
   const size_t vbase = (size_t)dict * M + v0;
   const Shared sh{s_reg, s_above, s_bcnt};
@@ -393,7 +473,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
     vs[k].lo32 = s_lo32[vs[k].vi];
     vs[k].hi32 = s_hi32[vs[k].vi];
   }
-  sweep<DT, D, PASS_COLLECT>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
+  sweep<DT, D, PASS_COLLECT, true>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
   __syncthreads();
 
   // ---- resolve boundaries; refine the rest (rare) -------------------------------------------
