@@ -41,7 +41,35 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB three times (a plain "
+                         "device copy of known size, for scaling memory-traffic counters)")
     return ap.parse_args()
+
+
+def measured_traffic(workload, select, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("record: "):
+                rec = json.loads(line[len("record: "):])
+    if rec is None or rec.get("select") != select or kernel not in rec:
+        return None
+    csrc = os.path.join(ROOT, "sparse_dictionary_coding_amd", "csrc")
+    src = {"select_kernel": "select.hip", "score_topn_kernel": "score_topn.hip"}[kernel]
+    h = hashlib.sha256()
+    for name in (src, "common.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec[kernel]["sources_sha256_16"]:
+        return None
+    return rec[kernel]["bytes"]
 
 
 def cpu_baseline(w, select, seconds):
@@ -129,6 +157,14 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -165,12 +201,12 @@ def main():
         ach = screen_flops / (stage_ms[0] * 1e-3) / 1e12
         roof = {"kernel": "score_topn_kernel", "bound": "mfma", "achieved": ach,
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": None}
+                "traffic": measured_traffic(w.name, args.select, "score_topn_kernel")}
     else:
         ach = sel_flops / (stage_ms[1] * 1e-3) / 1e12
         roof = {"kernel": "select_kernel", "bound": "alu", "achieved": ach,
                 "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / ALU_PEAK_TFLOPS,
-                "traffic": None}
+                "traffic": measured_traffic(w.name, args.select, "select_kernel")}
     # the screening kernel against HBM as well (the decode-step figure of merit)
     screen_gbs = screen_bytes / (stage_ms[0] * 1e-3) / 1e9
     trig = int((codes.flags & fadkv.FLAG_TRIGGER).ne(0).sum().item())
