@@ -163,6 +163,38 @@ int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *
 int fadkv_reconstruct(const fadkv_dict *dict, const int32_t *idx, const float *coef, int32_t s,
                       int64_t M, void *X_hat, int32_t out_dtype, hipStream_t stream);
 
+/* ---- decode attention over the codes ------------------------------------------------------
+ * The consumer of the encoder's output.  The abstract stores every token's key and value as a
+ * sparse combination of atoms, so a decode query meets the cached keys through the atoms:
+ * <q, k_t> = sum_k cK[t][k] <q, d^K_{iK[t][k]}> needs q . D_K^T once per query and s gathers
+ * per token, and the weighted values sum to w . D_V with w the softmax weights scattered onto
+ * the atoms.  The pages give no formula for this step; the definition taken is standard scaled
+ * softmax attention over the rebuilt tokens:
+ *   out[r][g] = sum_{t < len[r]} p_t v_t,  p = softmax_t(scale * <q[r][g], k_t>),
+ *   k_t = sum_k cK[r][t][k] d^K_{iK[r][t][k]}, v_t = sum_k cV[r][t][k] d^V_{iV[r][t][k]},
+ * and out[r][g] = 0 for a row without tokens.
+ *
+ * Layer `layer` takes its keys from dictionary 2*layer of `dict` and its values from 2*layer+1
+ * (0 <= layer, 2*layer + 1 < num_dicts).  Rows r < R are (KV head, sequence) pairs:
+ *   k_idx, v_idx  device int32 [R][T][s]  atom per slot; -1 (or anything outside [0, N)) = empty
+ *   k_coef, v_coef device fp32 [R][T][s]
+ *   lens          device int32 [R]        cached tokens of the row (clamped to [0, T])
+ *   q             device [R][G][d] in the dictionary dtype, 16-byte aligned; G query heads
+ *                 share row r's keys and values (1 <= G <= 64)
+ *   out           device fp32 [R][G][d], overwritten
+ *   scale         finite (e.g. 1/sqrt(d))
+ * 1 <= s <= 32, N <= 16384, R >= 0, T >= 0, R*G < 2^31.  Workspace: at least
+ * fadkv_attend_workspace_bytes() bytes, 256-byte aligned, caller-owned (it holds q . D_K^T and
+ * then the atom weights, fp32 [R*G][N]).  Checked synchronously; nothing is launched on error.
+ * fp32 throughout after the 16-bit products; the value weights are accumulated with LDS
+ * atomics, so the last bits of out may differ between runs. */
+int fadkv_attend_workspace_bytes(const fadkv_dict *dict, int64_t R, int32_t G, size_t *bytes);
+int fadkv_attend(const fadkv_dict *dict, int32_t layer, int32_t s, const int32_t *k_idx,
+                 const float *k_coef, const int32_t *v_idx, const float *v_coef,
+                 const int32_t *lens, int64_t R, int32_t T, const void *q, int32_t G,
+                 float scale, float *out, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *fadkv_status_string(int status);
 

@@ -12,6 +12,7 @@ namespace {
 constexpr int kMaxN = 65535;    // pool indices are stored as uint16
 constexpr int kMaxPool = 512;   // one selection thread per pool entry
 constexpr int kMaxS = 32;
+constexpr int kMaxAttendN = 16384;   // a query's q . D_K^T row and atom weights live in LDS
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -219,6 +220,51 @@ int fadkv_reconstruct(const fadkv_dict *dict, const int32_t *idx, const float *c
     return FADKV_ERR_ARG;
   if (fadkv::launch_reconstruct(dict->dtype, dict->d, dict->atoms, idx, coef, dict->num_dicts,
                                 dict->N, (int)M, s, X_hat, out_dtype, stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_attend_workspace_bytes(const fadkv_dict *dict, int64_t R, int32_t G, size_t *bytes) {
+  if (!bytes || !dict) return FADKV_ERR_ARG;
+  if (dict->dtype != FADKV_F32 && dict->dtype != FADKV_F16 && dict->dtype != FADKV_BF16)
+    return FADKV_ERR_DTYPE;
+  if (dict->num_dicts < 2 || dict->N < 1 || dict->N > kMaxAttendN ||
+      (dict->d != 64 && dict->d != 128))
+    return FADKV_ERR_SHAPE;
+  if (R < 0 || G < 1 || G > 64) return FADKV_ERR_SHAPE;
+  if ((double)R * (double)G >= 2147483648.0) return FADKV_ERR_SHAPE;
+  *bytes = align_up((size_t)R * (size_t)G * (size_t)dict->N * sizeof(float));
+  return FADKV_OK;
+}
+
+int fadkv_attend(const fadkv_dict *dict, int32_t layer, int32_t s, const int32_t *k_idx,
+                 const float *k_coef, const int32_t *v_idx, const float *v_coef,
+                 const int32_t *lens, int64_t R, int32_t T, const void *q, int32_t G,
+                 float scale, float *out, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  if (dict->N > kMaxAttendN) return FADKV_ERR_SHAPE;
+  if (layer < 0 || 2 * (int64_t)layer + 1 >= dict->num_dicts) return FADKV_ERR_SHAPE;
+  if (s < 1 || s > kMaxS || R < 0 || T < 0 || G < 1 || G > 64) return FADKV_ERR_SHAPE;
+  if ((double)R * (double)G >= 2147483648.0) return FADKV_ERR_SHAPE;
+  if ((double)R * (double)T * (double)s >= 9.0e18) return FADKV_ERR_SHAPE;
+  if (!isfinite(scale)) return FADKV_ERR_ARG;
+  if (R == 0) return FADKV_OK;
+  if (!lens || !q || !out || !aligned(lens, 4) || !aligned(q, 16) || !aligned(out, 4))
+    return FADKV_ERR_ARG;
+  if (T > 0 && (!k_idx || !k_coef || !v_idx || !v_coef || !aligned(k_idx, 4) ||
+                !aligned(k_coef, 4) || !aligned(v_idx, 4) || !aligned(v_coef, 4)))
+    return FADKV_ERR_ARG;
+  const size_t need = align_up((size_t)R * (size_t)G * (size_t)dict->N * sizeof(float));
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need)
+    return FADKV_ERR_WORKSPACE;
+  const size_t esize = dict->dtype == FADKV_F32 ? 4 : 2;
+  const size_t dict_bytes = (size_t)dict->N * (size_t)dict->d * esize;
+  const uint8_t *atoms = static_cast<const uint8_t *>(dict->atoms);
+  if (fadkv::launch_attend(dict->dtype, dict->d, atoms + (size_t)(2 * layer) * dict_bytes,
+                           atoms + (size_t)(2 * layer + 1) * dict_bytes, dict->N, s, k_idx, k_coef,
+                           v_idx, v_coef, lens, (int)R, T, q, G, scale, out,
+                           static_cast<float *>(workspace), stream) != hipSuccess)
     return FADKV_ERR_HIP;
   return FADKV_OK;
 }

@@ -27,4 +27,11 @@ hipError_t launch_reconstruct(int dtype, int d, const void *atoms, const int32_t
                               const float *coef, int num_dicts, int N, int M, int s, void *out,
                               int out_dtype, hipStream_t stream);
 
+// decode attention over the codes: qd = Q D_K^T (and out = 0), per-row softmax scattering the
+// value weights onto the atoms (in place over qd), out += weights . D_V
+hipError_t launch_attend(int dtype, int d, const void *dictK, const void *dictV, int N, int s,
+                         const int32_t *k_idx, const float *k_coef, const int32_t *v_idx,
+                         const float *v_coef, const int32_t *lens, int R, int T, const void *q,
+                         int G, float scale, float *out, float *ws, hipStream_t stream);
+
 }  // namespace fadkv

@@ -87,6 +87,16 @@ def lib() -> ctypes.CDLL:
         h.fadkv_reconstruct.argtypes = [P(fadkv_dict), ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_void_p]
+        h.fadkv_attend_workspace_bytes.restype = ctypes.c_int
+        h.fadkv_attend_workspace_bytes.argtypes = [P(fadkv_dict), ctypes.c_int64, ctypes.c_int32,
+                                                   P(ctypes.c_size_t)]
+        h.fadkv_attend.restype = ctypes.c_int
+        h.fadkv_attend.argtypes = [P(fadkv_dict), ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
         _lib_handle = h
     return _lib_handle
 
@@ -290,4 +300,47 @@ def fadkv_reconstruct(atoms: torch.Tensor, idx: torch.Tensor, coef: torch.Tensor
                                  out.data_ptr(), _DT[out.dtype], _stream(stream))
     if st != FADKV_OK:
         raise FadkvError("fadkv_reconstruct", st)
+    return out
+
+
+def fadkv_attend_workspace_bytes(atoms: torch.Tensor, R: int, G: int) -> int:
+    T, N, d = atoms.shape
+    dd = fadkv_dict(T, N, d, _DT[atoms.dtype], None, None)
+    out = ctypes.c_size_t(0)
+    st = lib().fadkv_attend_workspace_bytes(ctypes.byref(dd), int(R), int(G), ctypes.byref(out))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_attend_workspace_bytes", st)
+    return int(out.value)
+
+
+def fadkv_attend(atoms: torch.Tensor, layer: int, k_idx: torch.Tensor, k_coef: torch.Tensor,
+                 v_idx: torch.Tensor, v_coef: torch.Tensor, lens: torch.Tensor, q: torch.Tensor,
+                 scale: float, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention of q [R][G][d] over the sparse-coded keys/values of `layer` (codes
+    [R][T][s], lens [R]); returns (or fills) out [R][G][d] fp32."""
+    dd = _dict(atoms)
+    _check(k_idx, "k_idx", torch.int32)
+    R, T, s = k_idx.shape
+    _check(k_coef, "k_coef", torch.float32, (R, T, s))
+    _check(v_idx, "v_idx", torch.int32, (R, T, s))
+    _check(v_coef, "v_coef", torch.float32, (R, T, s))
+    _check(lens, "lens", torch.int32, (R,))
+    _check(q, "q", atoms.dtype)
+    if q.dim() != 3 or q.shape[0] != R or q.shape[2] != atoms.shape[2]:
+        raise ValueError(f"q must be [{R}][G][{atoms.shape[2]}]")
+    G = q.shape[1]
+    if out is None:
+        out = torch.empty(R, G, atoms.shape[2], dtype=torch.float32, device=atoms.device)
+    _check(out, "out", torch.float32, (R, G, atoms.shape[2]))
+    if workspace is None:
+        workspace = torch.empty(max(1, fadkv_attend_workspace_bytes(atoms, R, G)),
+                                dtype=torch.uint8, device=atoms.device)
+    st = lib().fadkv_attend(ctypes.byref(dd), int(layer), int(s), k_idx.data_ptr(),
+                            k_coef.data_ptr(), v_idx.data_ptr(), v_coef.data_ptr(),
+                            lens.data_ptr(), int(R), int(T), q.data_ptr(), int(G), float(scale),
+                            out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                            _stream(stream))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_attend", st)
     return out

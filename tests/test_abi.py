@@ -150,3 +150,37 @@ def test_reconstruct_argument_checks():
     assert rec(_dict(), s=40) == -3
     assert rec(_dict(), odt=9) == -2
     assert rec(_dict(), M=0) == 0
+
+
+def test_attend_argument_checks():
+    L = fadkv.lib()
+
+    def att(dd, layer=0, s=8, ptrs=FAKE, lens=FAKE, R=16, T=100, q=FAKE, G=3, scale=0.1,
+            out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return L.fadkv_attend(ctypes.byref(dd), layer, s, ptrs, ptrs, ptrs, ptrs, lens, R, T, q,
+                              G, scale, out, ws, ws_bytes, None)
+
+    assert att(_dict(num_dicts=2, N=1024), layer=1) == -3           # needs dictionaries 2 and 3
+    assert att(_dict(num_dicts=2, N=32768)) == -3                   # N above the LDS budget
+    assert att(_dict(), s=0) == -3
+    assert att(_dict(), s=33) == -3
+    assert att(_dict(), G=0) == -3
+    assert att(_dict(), G=65) == -3
+    assert att(_dict(), R=-1) == -3
+    assert att(_dict(), scale=float("inf")) == -1
+    assert att(_dict(), q=FAKE + 4) == -1                           # q must be 16-byte aligned
+    assert att(_dict(), lens=None) == -1
+    assert att(_dict(), ptrs=None) == -1
+    assert att(_dict(), ws_bytes=16) == -4
+    assert att(_dict(), ws=FAKE + 16) == -4
+    assert att(_dict(), R=0, ptrs=None, lens=None, q=None, out=None, ws=None, ws_bytes=0) == 0
+
+
+def test_attend_workspace_size():
+    L = fadkv.lib()
+    out = ctypes.c_size_t(0)
+    assert L.fadkv_attend_workspace_bytes(ctypes.byref(_dict(num_dicts=2, N=4096)), 256, 3,
+                                          ctypes.byref(out)) == 0
+    assert out.value >= 256 * 3 * 4096 * 4 and out.value % 256 == 0
+    assert L.fadkv_attend_workspace_bytes(ctypes.byref(_dict(num_dicts=1)), 1, 1,
+                                          ctypes.byref(out)) == -3
