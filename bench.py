@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--path", default="encode", choices=["encode", "attend"],
+                    help="encode: the encoder hot path (default); attend: decode attention of "
+                         "one layer over the sparse codes")
+    ap.add_argument("--tokens", type=int, default=2048, help="cached tokens per row (--path attend)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB three times (a plain "
                          "device copy of known size, for scaling memory-traffic counters)")
@@ -108,6 +112,102 @@ def cpu_baseline(w, select, seconds):
                       f"(encode + adapt, NumPy fp64), {dt:.1f} s"}
 
 
+def bench_attend(args):
+    """Decode attention of one layer over its sparse-coded cache: R = KV heads x sequences rows
+    of `--tokens` tokens, each coded by this library's encoder from synthetic K/V vectors, and G
+    query heads per KV head.  Prints one JSON line; `value` is query-token pairs per second."""
+    import numpy as np
+    import torch
+
+    from sparse_dictionary_coding_amd import fadkv, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    heads, seqs, G = 8, w.M // 8, 3        # Llama-3.2-3B: 8 KV heads, 3 query heads per KV head
+    R, T, d, N, s = heads * seqs, args.tokens, w.d, w.N, w.s
+    gen = synth.SyntheticKV(w, device=dev, num_dicts=2)
+    atoms = gen.atoms()                    # dictionary 0 = keys, 1 = values of the layer
+    p = fadkv.Params(n=w.n, s=s)
+    X = gen.batch(atoms, M=R * T)
+    codes = fadkv.fadkv_encode(atoms, X, p)
+    del X
+    ki = codes.idx[0].reshape(R, T, s).contiguous()
+    kc = codes.coef[0].reshape(R, T, s).contiguous()
+    vi = codes.idx[1].reshape(R, T, s).contiguous()
+    vc = codes.coef[1].reshape(R, T, s).contiguous()
+    lens = torch.full((R,), T, dtype=torch.int32, device=dev)
+    q = torch.randn(R, G, d, device=dev).to(atoms.dtype)
+    out = torch.empty(R, G, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(fadkv.fadkv_attend_workspace_bytes(atoms, R, G), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(d))
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fadkv.fadkv_attend(atoms, 0, ki, kc, vi, vc, lens, q, scale, out=out, workspace=ws,
+                           stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fadkv.fadkv_attend(atoms, 0, ki, kc, vi, vc, lens, q, scale, out=out, workspace=ws,
+                           stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    esize = atoms.element_size()
+    code_bytes = 2 * R * T * s * 8
+    alg_bytes = code_bytes + 2 * N * d * esize + R * G * d * (esize + 4)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    # context: dense attention over the rebuilt cache (what the codes replace)
+    K = fadkv.fadkv_reconstruct(atoms[0:1], ki.view(1, R * T, s), kc.view(1, R * T, s)).view(R, T, d)
+    V = fadkv.fadkv_reconstruct(atoms[1:2], vi.view(1, R * T, s), vc.view(1, R * T, s)).view(R, T, d)
+    for _ in range(3):
+        torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=scale)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=scale)
+    b.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = a.elapsed_time(b) / args.steps
+    res = {
+        "metric": "decode attention over sparse-coded KV: query-token pairs/s",
+        "value": R * G * T * args.steps / wall, "unit": "query-token pairs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} attention, one layer", "rows": R, "kv_heads": heads,
+                   "sequences": seqs, "query_heads_per_kv_head": G, "tokens": T, "N": N, "s": s,
+                   "d": d},
+        "roofline": {"kernel": "fadkv_attend (3 kernels)", "bound": "hbm", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+        "attend_ms": ms, "algorithmic_bytes": alg_bytes, "code_bytes": code_bytes,
+        "dense_sdpa_ms": dense_ms, "dense_kv_bytes": 2 * R * T * d * esize,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import attend_oracle
+        A = atoms.double().cpu().numpy()
+        kin, kcn, vin, vcn = (t.cpu().numpy() for t in (ki, kc, vi, vc))
+        qn = q.double().cpu().numpy()
+        t1 = time.perf_counter()
+        rows = 0
+        while time.perf_counter() - t1 < args.cpu_seconds and rows < R:
+            attend_oracle.attend_row(A[0], A[1], kin[rows], kcn[rows], vin[rows], vcn[rows],
+                                     qn[rows], scale)
+            rows += 1
+        dt = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": rows * G * T / dt, "unit": "query-token pairs/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} of {R} rows x {G} queries x {T} tokens "
+                                         f"(NumPy fp64, Python loops), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -115,6 +215,9 @@ def main():
               "(dictionaries shard by layer with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.path == "attend":
+        bench_attend(args)
+        return
 
     import torch
 

@@ -184,10 +184,11 @@ int fadkv_reconstruct(const fadkv_dict *dict, const int32_t *idx, const float *c
  *   out           device fp32 [R][G][d], overwritten
  *   scale         finite (e.g. 1/sqrt(d))
  * 1 <= s <= 32, N <= 16384, R >= 0, T >= 0, R*G < 2^31.  Workspace: at least
- * fadkv_attend_workspace_bytes() bytes, 256-byte aligned, caller-owned (it holds q . D_K^T and
- * then the atom weights, fp32 [R*G][N]).  Checked synchronously; nothing is launched on error.
- * fp32 throughout after the 16-bit products; the value weights are accumulated with LDS
- * atomics, so the last bits of out may differ between runs. */
+ * fadkv_attend_workspace_bytes() bytes, 256-byte aligned, caller-owned (it holds q . D_K^T,
+ * then the atom weights, fp32 [R*G][N], and partial outputs per range of 128 atoms, fp32
+ * [ceil(N/128)][R*G][d]).  Checked synchronously; nothing is launched on error.  fp32
+ * throughout after the 16-bit products; the value weights are accumulated with LDS atomics,
+ * so the last bits of out may differ between runs. */
 int fadkv_attend_workspace_bytes(const fadkv_dict *dict, int64_t R, int32_t G, size_t *bytes);
 int fadkv_attend(const fadkv_dict *dict, int32_t layer, int32_t s, const int32_t *k_idx,
                  const float *k_coef, const int32_t *v_idx, const float *v_coef,

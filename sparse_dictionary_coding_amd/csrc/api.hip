@@ -81,6 +81,13 @@ int check_codes(const fadkv_codes *c) {
   return FADKV_OK;
 }
 
+// q . D_K^T, then the atom weights, [R*G][N] fp32; then [ranges of 128 atoms][R*G][d] fp32
+size_t attend_ws_bytes(const fadkv_dict *dict, int64_t R, int32_t G) {
+  const size_t RG = (size_t)R * (size_t)G;
+  const size_t ranges = ((size_t)dict->N + 127) / 128;
+  return align_up(RG * (size_t)dict->N * sizeof(float) + ranges * RG * (size_t)dict->d * sizeof(float));
+}
+
 #define FADKV_TRY(expr)        \
   do {                         \
     const int _st = (expr);    \
@@ -233,7 +240,7 @@ int fadkv_attend_workspace_bytes(const fadkv_dict *dict, int64_t R, int32_t G, s
     return FADKV_ERR_SHAPE;
   if (R < 0 || G < 1 || G > 64) return FADKV_ERR_SHAPE;
   if ((double)R * (double)G >= 2147483648.0) return FADKV_ERR_SHAPE;
-  *bytes = align_up((size_t)R * (size_t)G * (size_t)dict->N * sizeof(float));
+  *bytes = attend_ws_bytes(dict, R, G);
   return FADKV_OK;
 }
 
@@ -255,7 +262,7 @@ int fadkv_attend(const fadkv_dict *dict, int32_t layer, int32_t s, const int32_t
   if (T > 0 && (!k_idx || !k_coef || !v_idx || !v_coef || !aligned(k_idx, 4) ||
                 !aligned(k_coef, 4) || !aligned(v_idx, 4) || !aligned(v_coef, 4)))
     return FADKV_ERR_ARG;
-  const size_t need = align_up((size_t)R * (size_t)G * (size_t)dict->N * sizeof(float));
+  const size_t need = attend_ws_bytes(dict, R, G);
   if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need)
     return FADKV_ERR_WORKSPACE;
   const size_t esize = dict->dtype == FADKV_F32 ? 4 : 2;

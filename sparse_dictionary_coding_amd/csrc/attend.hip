@@ -4,12 +4,13 @@
 // with qd = D_K q computed once per query, and sum_t p_t v_t = w . D_V with the softmax weights
 // scattered onto the value atoms, w[j] = sum_{t,k: iV[t][k] = j} p_t cV[t][k].  Three kernels:
 //   attend_qd       qd[query][j] = <q, d^K_j>: v_mfma_f32_16x16x32 (16x16x4 for fp32), 64 queries
-//                   x 512 atoms per workgroup; also clears out[]
+//                   x 128 atoms per workgroup
 //   attend_softmax  one workgroup per (row, query group): qd rows in LDS, a max pass and an
 //                   exp/sum/scatter pass over the row's tokens (s LDS gathers per token and
 //                   query, fp32 LDS atomics onto w), then w / sum written over qd
-//   attend_out      out[query] += w[query][j0:j1] . D_V[j0:j1] for 16 queries x 256 atoms per
-//                   workgroup (fp32, global atomics across atom ranges)
+//   attend_out      part[range][query] = w[query][range] . D_V[range] for 32 queries x 128 atoms
+//                   per workgroup (fp32 register tiles over LDS-staged chunks)
+//   attend_reduce   out = sum over the ranges of part
 #include "common.h"
 #include "kernels.h"
 
@@ -41,12 +42,13 @@ __device__ __forceinline__ void mfma_chunk(const uint4 &a, const uint4 &b, float
 }
 
 constexpr int QD_QUERIES = 64;     // four 16-query blocks
-constexpr int QD_ATOMS = 512;      // 32 tiles of 16 atoms, eight per wave
-constexpr int SM_THREADS = 256;
+constexpr int QD_ATOMS = 128;      // 8 tiles of 16 atoms, two per wave
+constexpr int SM_THREADS = 1024;   // 16 waves: four per SIMD hide the code loads
 constexpr int SM_GMAX = 8;         // queries per softmax workgroup
+constexpr int SM_CH = 8;           // slots loaded together
 constexpr int SM_LDS_FLOATS = 32768;   // qd rows + weights: 128 KB
-constexpr int OUT_QUERIES = 16;
-constexpr int OUT_ATOMS = 256;
+constexpr int OUT_QUERIES = 32;
+constexpr int OUT_ATOMS = 128;
 
 }  // namespace
 
@@ -56,18 +58,11 @@ constexpr int OUT_ATOMS = 256;
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attend_qd_kernel(const uint8_t *__restrict__ dictK,
                                                         const uint8_t *__restrict__ Q, int RG,
-                                                        int N, float *__restrict__ qd,
-                                                        float *__restrict__ out) {
+                                                        int N, float *__restrict__ qd) {
   using G = AGeo<DT, D>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q0 = blockIdx.x * QD_QUERIES;
   const int r16 = lane & 15, g4 = lane >> 4;
-  if (blockIdx.y == 0) {   // out is accumulated by attend_out
-    for (int i = threadIdx.x; i < QD_QUERIES * D; i += blockDim.x) {
-      const int qq = q0 + i / D;
-      if (qq < RG) out[(size_t)qq * D + i % D] = 0.f;
-    }
-  }
   uint4 b[4][G::CH];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -99,10 +94,62 @@ __global__ __launch_bounds__(256) void attend_qd_kernel(const uint8_t *__restric
     for (int k = 0; k < 4; ++k) {
       const int qq = q0 + 16 * k + r16;
       if (qq >= RG) continue;
+      const int j = t * 16 + 4 * g4;
+      float *dst = qd + (size_t)qq * N + j;
+      if (j + 4 <= N && (N & 3) == 0) {
+        *reinterpret_cast<float4_t *>(dst) = acc[k];
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = t * 16 + 4 * g4 + e;
-        if (j < N) qd[(size_t)qq * N + j] = acc[k][e];
+        for (int e = 0; e < 4; ++e)
+          if (j + e < N) dst[e] = acc[k][e];
+      }
+    }
+  }
+}
+
+// up to SM_CH slots of a token (rem = slots left); 16-byte loads when every token's slots start
+// 16-byte aligned (s a multiple of 4), else 4-byte loads.  Missing slots read as empty.
+__device__ __forceinline__ void load_slots(const int32_t *__restrict__ idx,
+                                           const float *__restrict__ coef, int rem, bool vec,
+                                           int (&j)[SM_CH], float (&c)[SM_CH]) {
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < SM_CH / 4; ++q) {
+      int4 iv = make_int4(-1, -1, -1, -1);
+      float4 cv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * q < rem) {
+        iv = reinterpret_cast<const int4 *>(idx)[q];
+        cv = reinterpret_cast<const float4 *>(coef)[q];
+      }
+      j[4 * q] = iv.x; j[4 * q + 1] = iv.y; j[4 * q + 2] = iv.z; j[4 * q + 3] = iv.w;
+      c[4 * q] = cv.x; c[4 * q + 1] = cv.y; c[4 * q + 2] = cv.z; c[4 * q + 3] = cv.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < SM_CH; ++k) {
+      j[k] = k < rem ? idx[k] : -1;
+      c[k] = k < rem ? coef[k] : 0.f;
+    }
+  }
+}
+
+// z[g] = sum_k coef[k] qs[g][idx[k]] over the token's valid slots; the slots are loaded SM_CH
+// at a time before their gathers, so those loads are in flight together.
+__device__ __forceinline__ void logits(const int32_t *__restrict__ idx,
+                                       const float *__restrict__ coef, int s, int N, int gn,
+                                       const float *qs, float (&z)[SM_GMAX]) {
+#pragma unroll
+  for (int g = 0; g < SM_GMAX; ++g) z[g] = 0.f;
+  for (int k0 = 0; k0 < s; k0 += SM_CH) {
+    int j[SM_CH];
+    float c[SM_CH];
+    load_slots(idx + k0, coef + k0, s - k0, (s & 3) == 0, j, c);
+#pragma unroll
+    for (int k = 0; k < SM_CH; ++k) {
+      if (j[k] >= 0 && j[k] < N) {
+#pragma unroll
+        for (int g = 0; g < SM_GMAX; ++g)
+          if (g < gn) z[g] = fmaf(c[k], qs[g * N + j[k]], z[g]);
       }
     }
   }
@@ -139,16 +186,7 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
   for (int g = 0; g < SM_GMAX; ++g) mx[g] = -__builtin_inff();
   for (int t = tid; t < L; t += SM_THREADS) {
     float z[SM_GMAX];
-#pragma unroll
-    for (int g = 0; g < SM_GMAX; ++g) z[g] = 0.f;
-    for (int k = 0; k < s; ++k) {
-      const int j = k_idx[cbase + (size_t)t * s + k];
-      if (j < 0 || j >= N) continue;
-      const float c = k_coef[cbase + (size_t)t * s + k];
-#pragma unroll
-      for (int g = 0; g < SM_GMAX; ++g)
-        if (g < gn) z[g] = fmaf(c, qs[g * N + j], z[g]);
-    }
+    logits(k_idx + cbase + (size_t)t * s, k_coef + cbase + (size_t)t * s, s, N, gn, qs, z);
 #pragma unroll
     for (int g = 0; g < SM_GMAX; ++g) mx[g] = fmaxf(mx[g], z[g] * scale);
   }
@@ -175,30 +213,27 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
     sum[g] = 0.f;
   }
   for (int t = tid; t < L; t += SM_THREADS) {
+    const size_t o = cbase + (size_t)t * s;
     float z[SM_GMAX];
-#pragma unroll
-    for (int g = 0; g < SM_GMAX; ++g) z[g] = 0.f;
-    for (int k = 0; k < s; ++k) {
-      const int j = k_idx[cbase + (size_t)t * s + k];
-      if (j < 0 || j >= N) continue;
-      const float c = k_coef[cbase + (size_t)t * s + k];
-#pragma unroll
-      for (int g = 0; g < SM_GMAX; ++g)
-        if (g < gn) z[g] = fmaf(c, qs[g * N + j], z[g]);
-    }
+    logits(k_idx + o, k_coef + o, s, N, gn, qs, z);
     float p[SM_GMAX];
 #pragma unroll
     for (int g = 0; g < SM_GMAX; ++g) {
       p[g] = g < gn ? __expf(z[g] * scale - m[g]) : 0.f;
       sum[g] += p[g];
     }
-    for (int k = 0; k < s; ++k) {
-      const int j = v_idx[cbase + (size_t)t * s + k];
-      if (j < 0 || j >= N) continue;
-      const float c = v_coef[cbase + (size_t)t * s + k];
+    for (int k0 = 0; k0 < s; k0 += SM_CH) {
+      int vj[SM_CH];
+      float vcf[SM_CH];
+      load_slots(v_idx + o + k0, v_coef + o + k0, s - k0, (s & 3) == 0, vj, vcf);
 #pragma unroll
-      for (int g = 0; g < SM_GMAX; ++g)
-        if (g < gn) atomicAdd(&wv[g * N + j], p[g] * c);
+      for (int k = 0; k < SM_CH; ++k) {
+        if (vj[k] >= 0 && vj[k] < N) {
+#pragma unroll
+          for (int g = 0; g < SM_GMAX; ++g)
+            if (g < gn) atomicAdd(&wv[g * N + vj[k]], p[g] * vcf[k]);
+        }
+      }
     }
   }
 #pragma unroll
@@ -220,36 +255,83 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
   }
 }
 
-// out[query][:] += sum_{j in this workgroup's atom range} w[query][j] d^V_j: thread (query
-// qi = tid / 16, part dp = tid % 16) owns D / 16 consecutive output elements.
+// part[range][query][:] = sum_{j in the range} w[query][j] d^V_j.  A workgroup takes
+// OUT_QUERIES queries x OUT_ATOMS atoms; 32-atom chunks of w (stored atom-major) and of D_V (as
+// fp32) are staged in LDS, and thread (tq, td) accumulates a 4-query x 4-element register tile
+// from one 16-byte read of each per atom.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attend_out_kernel(const uint8_t *__restrict__ dictV,
                                                          const float *__restrict__ w, int RG,
-                                                         int N, float *__restrict__ out) {
-  constexpr int DP = D / 16;
-  constexpr int ROWB = D * Elem<DT>::bytes;
-  const int qq = blockIdx.x * OUT_QUERIES + threadIdx.x / 16;
-  const int dp = threadIdx.x % 16;
-  if (qq >= RG) return;
+                                                         int N, float *__restrict__ part_all) {
+  constexpr int CK = 32;                  // atoms per staged chunk
+  constexpr int QB = OUT_QUERIES;         // 32 queries: 8 thread rows of 4
+  constexpr int TD = D / 4;               // thread columns of 4 elements (32 or 16)
+  constexpr int TQ = 256 / TD;            // thread rows (8 or 16)
+  constexpr int QT = QB / TQ;             // queries per thread (4 or 2)
+  __shared__ __attribute__((aligned(16))) float s_w[CK][QB];
+  __shared__ __attribute__((aligned(16))) float s_v[CK][D];
+  const int tid = threadIdx.x;
+  const int tq = tid / TD, td = tid % TD;
+  const int q0 = blockIdx.x * QB;
   const int j0 = blockIdx.y * OUT_ATOMS;
   const int j1 = min(N, j0 + OUT_ATOMS);
-  float acc[DP];
+  float acc[QT][4];
 #pragma unroll
-  for (int i = 0; i < DP; ++i) acc[i] = 0.f;
-  const float *wrow = w + (size_t)qq * N;
-  for (int j = j0; j < j1; ++j) {
-    const float wj = wrow[j];
-    const uint8_t *src = dictV + (size_t)j * ROWB + dp * DP * Elem<DT>::bytes;
+  for (int i = 0; i < QT; ++i)
 #pragma unroll
-    for (int i = 0; i < DP; ++i) acc[i] = fmaf(wj, elem_f<DT>(src, i), acc[i]);
+    for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+  for (int c0 = j0; c0 < j1; c0 += CK) {
+    for (int i = tid; i < QB * CK; i += 256) {
+      const int qi = i / CK, a = i % CK;
+      const int qq = q0 + qi, j = c0 + a;
+      s_w[a][qi] = (qq < RG && j < j1) ? w[(size_t)qq * N + j] : 0.f;
+    }
+    for (int i = tid; i < CK * D; i += 256) {
+      const int a = i / D, e = i % D;
+      const int j = c0 + a;
+      s_v[a][e] = j < j1 ? elem_f<DT>(dictV + (size_t)j * D * Elem<DT>::bytes, e) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int a = 0; a < CK; ++a) {
+      float wq[QT];
+#pragma unroll
+      for (int i = 0; i < QT; ++i) wq[i] = s_w[a][QT * tq + i];
+      const float4 dv = *reinterpret_cast<const float4 *>(&s_v[a][4 * td]);
+#pragma unroll
+      for (int i = 0; i < QT; ++i) {
+        acc[i][0] = fmaf(wq[i], dv.x, acc[i][0]);
+        acc[i][1] = fmaf(wq[i], dv.y, acc[i][1]);
+        acc[i][2] = fmaf(wq[i], dv.z, acc[i][2]);
+        acc[i][3] = fmaf(wq[i], dv.w, acc[i][3]);
+      }
+    }
+    __syncthreads();
   }
+  float *part = part_all + (size_t)blockIdx.y * RG * D;
 #pragma unroll
-  for (int i = 0; i < DP; ++i) atomicAdd(&out[(size_t)qq * D + dp * DP + i], acc[i]);
+  for (int i = 0; i < QT; ++i) {
+    const int qq = q0 + QT * tq + i;
+    if (qq >= RG) continue;
+    *reinterpret_cast<float4 *>(&part[(size_t)qq * D + 4 * td]) =
+        make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
+}
+
+// out[i] = sum over the atom ranges of part[range][i]
+__global__ __launch_bounds__(256) void attend_reduce_kernel(const float *__restrict__ part,
+                                                            int nranges, size_t total,
+                                                            float *__restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  float acc = 0.f;
+  for (int r = 0; r < nranges; ++r) acc += part[(size_t)r * total + i];
+  out[i] = acc;
 }
 
 #define FADKV_ATT_INST(DT, D)                                                                  \
   template __global__ void attend_qd_kernel<DT, D>(const uint8_t *, const uint8_t *, int, int, \
-                                                   float *, float *);                         \
+                                                   float *);                                  \
   template __global__ void attend_out_kernel<DT, D>(const uint8_t *, const float *, int, int,  \
                                                     float *);
 FADKV_ATT_INST(DT_F32, 64)
@@ -280,13 +362,18 @@ hipError_t launch_attend(int dtype, int d, const void *dictK, const void *dictV,
                                              (int)(SM_LDS_FLOATS * sizeof(float)));
     if (e != hipSuccess) return e;
   }
-  dim3 g3((unsigned)((RG + OUT_QUERIES - 1) / OUT_QUERIES), (unsigned)((N + OUT_ATOMS - 1) / OUT_ATOMS));
+  const int nranges = (N + OUT_ATOMS - 1) / OUT_ATOMS;
+  dim3 g3((unsigned)((RG + OUT_QUERIES - 1) / OUT_QUERIES), (unsigned)nranges);
+  float *part = ws + (size_t)RG * N;          // [nranges][RG][d] partial sums
+  const size_t total = (size_t)RG * d;
+  dim3 g4((unsigned)((total + 255) / 256));
 #define L(DT, D)                                                                                \
   do {                                                                                          \
-    hipLaunchKernelGGL((attend_qd_kernel<DT, D>), g1, dim3(256), 0, stream, K, Q, RG, N, ws, out); \
+    hipLaunchKernelGGL((attend_qd_kernel<DT, D>), g1, dim3(256), 0, stream, K, Q, RG, N, ws);    \
     hipLaunchKernelGGL(attend_softmax_kernel, g2, dim3(SM_THREADS), lds2, stream, k_idx, k_coef, \
                        v_idx, v_coef, lens, T, s, N, G, gw, scale, ws);                         \
-    hipLaunchKernelGGL((attend_out_kernel<DT, D>), g3, dim3(256), 0, stream, V, ws, RG, N, out); \
+    hipLaunchKernelGGL((attend_out_kernel<DT, D>), g3, dim3(256), 0, stream, V, ws, RG, N, part); \
+    hipLaunchKernelGGL(attend_reduce_kernel, g4, dim3(256), 0, stream, part, nranges, total, out); \
   } while (0)
   if (dtype == DT_F32) { if (d == 64) L(DT_F32, 64); else L(DT_F32, 128); }
   else if (dtype == DT_F16) { if (d == 64) L(DT_F16, 64); else L(DT_F16, 128); }
