@@ -299,6 +299,30 @@ def encode(atoms: np.ndarray, X: np.ndarray, p: OracleParams,
 # a6  fixed-size adaptation
 # ----------------------------------------------------------------------------------------
 
+def _commit_nontriggering(usage: np.ndarray, idx: np.ndarray, trig: np.ndarray):
+    """usage[j] += 1 for each atom of each non-triggering code (row order)."""
+    for m in range(idx.shape[0]):
+        if not trig[m]:
+            for j in idx[m]:
+                if j >= 0:
+                    usage[j] += 1
+
+
+def _recode_onto_new_atom(A, usage, j, x, idx_m, coef_m, p: OracleParams, dtype: str) -> float:
+    """Write the new atom round(x/||x||) into slot j (usage 1) and re-code the row onto it with
+    the one-atom ridge coefficient <d_j,x>/((1+rel) G_jj + abs); returns the new error."""
+    a = round_to_storage(x / np.sqrt(np.dot(x, x)), dtype)
+    A[j] = a
+    usage[j] = 1
+    g = float(np.dot(a, a))
+    c = float(np.dot(a, x)) / ((1.0 + p.ridge_rel) * g + p.ridge_abs)
+    idx_m[:] = -1
+    coef_m[:] = 0.0
+    idx_m[0] = j
+    coef_m[0] = c
+    return float(np.linalg.norm(x - c * a) / np.linalg.norm(x))
+
+
 def adapt_dictionary(A: np.ndarray, usage: np.ndarray, X: np.ndarray, idx: np.ndarray,
                      coef: np.ndarray, relerr: np.ndarray, flags: np.ndarray,
                      p: OracleParams, dtype: str):
@@ -324,11 +348,7 @@ def adapt_dictionary(A: np.ndarray, usage: np.ndarray, X: np.ndarray, idx: np.nd
         for j in idx[m]:
             if j >= 0:
                 touched[j] = True
-    for m in range(M):
-        if not trig[m]:
-            for j in idx[m]:
-                if j >= 0:
-                    usage[j] += 1
+    _commit_nontriggering(usage, idx, trig)
     eligible = [j for j in range(N) if usage[j] < p.tau_c and not touched[j]]
     cand = sorted(eligible, key=lambda j: (usage[j], j))
     replaced = np.full(M, -1, dtype=np.int32)
@@ -339,17 +359,7 @@ def adapt_dictionary(A: np.ndarray, usage: np.ndarray, X: np.ndarray, idx: np.nd
         if k < len(cand):
             j = cand[k]
             k += 1
-            x = X[m]
-            a = round_to_storage(x / np.sqrt(np.dot(x, x)), dtype)
-            A[j] = a
-            usage[j] = 1
-            g = float(np.dot(a, a))
-            c = float(np.dot(a, x)) / ((1.0 + p.ridge_rel) * g + p.ridge_abs)
-            idx[m] = -1
-            coef[m] = 0.0
-            idx[m, 0] = j
-            coef[m, 0] = c
-            relerr[m] = float(np.linalg.norm(x - c * a) / np.linalg.norm(x))
+            relerr[m] = _recode_onto_new_atom(A, usage, j, X[m], idx[m], coef[m], p, dtype)
             flags[m] |= FLAG_REPLACED
             replaced[m] = j
         else:
@@ -373,6 +383,64 @@ def adapt(atoms: np.ndarray, usage: np.ndarray, X: np.ndarray, codes: Codes,
         replaced[t] = adapt_dictionary(atoms[t], usage[t], X[t], codes.idx[t], codes.coef[t],
                                        codes.relerr[t], codes.flags[t], p, dtype)
     return atoms, usage, codes, replaced
+
+
+# ----------------------------------------------------------------------------------------
+# append-only growth (the contrast the abstract and Fig. 3a draw)
+# ----------------------------------------------------------------------------------------
+
+def append_dictionary(A: np.ndarray, usage: np.ndarray, X: np.ndarray, idx: np.ndarray,
+                      coef: np.ndarray, relerr: np.ndarray, flags: np.ndarray, n_atoms: int,
+                      p: OracleParams, dtype: str):
+    """Commit one step by appending instead of reusing: the abstract contrasts FAD-KV with
+    "naive append-only" adaptation, whose dictionary grows during generation (Fig. 3a).
+
+    The dictionary is stored with capacity A.shape[0]; its first n_atoms rows are in use and
+    the rest are zero (a zero atom scores 0 and is never selected).  Non-triggering rows commit
+    usage as in adapt_dictionary; the k-th triggering row (row order) appends round(x/||x||) at
+    slot n_atoms + k while the capacity lasts and is re-coded onto it exactly as a replacement
+    would be; rows past the capacity keep their code, commit its usage and are flagged
+    exhausted.  Arrays are modified in place; returns (replaced[M], new n_atoms).
+    """
+    cap = A.shape[0]
+    M = X.shape[0]
+    trig = (flags & FLAG_TRIGGER) != 0
+    _commit_nontriggering(usage, idx, trig)
+    replaced = np.full(M, -1, dtype=np.int32)
+    nxt = int(n_atoms)
+    for m in range(M):
+        if not trig[m]:
+            continue
+        if nxt < cap:
+            j = nxt
+            nxt += 1
+            relerr[m] = _recode_onto_new_atom(A, usage, j, X[m], idx[m], coef[m], p, dtype)
+            flags[m] |= FLAG_REPLACED
+            replaced[m] = j
+        else:
+            flags[m] |= FLAG_EXHAUSTED
+            for j in idx[m]:
+                if j >= 0:
+                    usage[j] += 1
+    return replaced, nxt
+
+
+def append(atoms: np.ndarray, usage: np.ndarray, X: np.ndarray, codes: Codes,
+           n_atoms: np.ndarray, p: OracleParams, dtype: str):
+    """append_dictionary over every dictionary; returns (atoms', usage', codes', replaced,
+    n_atoms')."""
+    atoms = np.array(atoms, dtype=np.float64, copy=True)
+    usage = np.array(usage, dtype=np.int64, copy=True)
+    X = np.asarray(X, dtype=np.float64)
+    codes = codes.copy()
+    n_atoms = np.array(n_atoms, dtype=np.int64, copy=True)
+    T, M = X.shape[0], X.shape[1]
+    replaced = np.full((T, M), -1, dtype=np.int32)
+    for t in range(T):
+        replaced[t], n_atoms[t] = append_dictionary(atoms[t], usage[t], X[t], codes.idx[t],
+                                                    codes.coef[t], codes.relerr[t],
+                                                    codes.flags[t], int(n_atoms[t]), p, dtype)
+    return atoms, usage, codes, replaced, n_atoms
 
 
 # ----------------------------------------------------------------------------------------

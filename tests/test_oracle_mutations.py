@@ -51,8 +51,8 @@ MUTATIONS = {
         ("return self.delta_key if dict_index % 2 == 0 else self.delta_value",
          "return self.delta_value if dict_index % 2 == 0 else self.delta_key"),
     "adapt commits triggering rows too":
-        ("    for m in range(M):\n        if not trig[m]:\n            for j in idx[m]:",
-         "    for m in range(M):\n        if True:\n            for j in idx[m]:"),
+        ("    for m in range(idx.shape[0]):\n        if not trig[m]:",
+         "    for m in range(idx.shape[0]):\n        if True:"),
     "adapt orders candidates by index only":
         ("cand = sorted(eligible, key=lambda j: (usage[j], j))", "cand = sorted(eligible)"),
     "adapt may take atoms selected this step":
@@ -70,6 +70,13 @@ MUTATIONS = {
     "reconstruct skips the first slot":
         ("            for k in range(s):\n                j = idx[t, m, k]",
          "            for k in range(1, s):\n                j = idx[t, m, k]"),
+    "append overwrites from slot 0":
+        ("    nxt = int(n_atoms)\n", "    nxt = 0\n"),
+    "append skips the usage commit":
+        ("    trig = (flags & FLAG_TRIGGER) != 0\n    _commit_nontriggering(usage, idx, trig)\n    replaced",
+         "    trig = (flags & FLAG_TRIGGER) != 0\n    replaced"),
+    "append ignores the capacity":
+        ("        if nxt < cap:\n", "        if nxt < cap + 1:\n"),
     "PL takes the pool head unsorted":
         ("    S = [int(j) for j in pool[order[:s]]]", "    S = [int(j) for j in pool[::-1][:s]]"),
 }

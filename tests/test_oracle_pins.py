@@ -517,6 +517,85 @@ def test_adapt_delta_extremes():
 
 
 # ---------------------------------------------------------------------------------------
+# append-only growth (the abstract's contrast; Fig. 3a)
+# ---------------------------------------------------------------------------------------
+
+def _append_run(steps=4, rows=64, cap_extra=400, seed=22, N=128, d=32, s=4, n=32, drift=0.25):
+    rng = np.random.default_rng(seed)
+    cap = N + cap_extra
+    atoms = np.zeros((1, cap, d))
+    atoms[0, :N] = oracle.round_to_storage(unit_rows(rng.standard_normal((N, d))), "f32")
+    usage = np.zeros((1, cap), dtype=np.int64)
+    n_atoms = np.array([N])
+    p = OracleParams(n=n, s=s)
+    hist = []
+    for step in range(steps):
+        X = np.empty((1, rows, d))
+        for m in range(rows):
+            if rng.uniform() < drift:
+                X[0, m] = rng.standard_normal(d)
+            else:
+                S = rng.choice(N, s, replace=False)
+                X[0, m] = rng.standard_normal(s) @ atoms[0, S]
+        X = oracle.round_to_storage(X, "f32")
+        codes = oracle.encode(atoms, X, p)
+        out = oracle.append(atoms, usage, X, codes, n_atoms, p, "f32")
+        hist.append((atoms, usage, n_atoms, X, codes) + out)
+        atoms, usage, _, _, n_atoms = out
+    return p, hist
+
+
+def test_append_grows_by_one_atom_per_trigger_in_row_order():
+    p, hist = _append_run()
+    committed = 0
+    for atoms, usage, n0, X, codes, na, nu, nc, rep, n1 in hist:
+        trig = np.flatnonzero(codes.flags[0] & FLAG_TRIGGER)
+        assert trig.size > 0
+        assert int(n1[0]) == int(n0[0]) + trig.size
+        assert list(rep[0][trig]) == list(range(int(n0[0]), int(n1[0])))
+        for m in trig:
+            x = X[0, m]
+            np.testing.assert_array_equal(na[0, rep[0, m]], oracle.round_to_storage(x / np.linalg.norm(x), "f32"))
+            assert nu[0, rep[0, m]] == 1 and nc.idx[0, m, 0] == rep[0, m]
+        np.testing.assert_array_equal(na[0, :int(n0[0])], atoms[0, :int(n0[0])])   # never overwrites
+        assert np.all(na[0, int(n1[0]):] == 0.0)
+        committed += int(np.sum(nc.idx >= 0))
+        assert int(nu.sum()) == committed
+
+
+def test_append_stops_at_capacity():
+    p, hist = _append_run(steps=1)
+    atoms, usage, n0, X, codes, *_ = hist[0]
+    trig = np.flatnonzero(codes.flags[0] & FLAG_TRIGGER)
+    assert trig.size > 2
+    small = atoms[:, : int(n0[0]) + 2]
+    na, nu, nc, rep, n1 = oracle.append(small, usage[:, : small.shape[1]], X, codes, n0, p, "f32")
+    assert int(n1[0]) == small.shape[1]
+    assert list(np.flatnonzero(rep[0] >= 0)) == list(trig[:2])
+    assert np.all(nc.flags[0][trig[2:]] & FLAG_EXHAUSTED)
+
+
+def test_append_and_replace_code_the_trigger_alike():
+    """The same step committed both ways: every triggering row gets the same one-atom code
+    (coefficient and error) whether its atom is appended or overwrites an inactive one."""
+    p, hist = _append_run(steps=1)
+    atoms, usage, n0, X, codes, na, nu, nc, rep, n1 = hist[0]
+    fa, fu, fc, frep = oracle.adapt(atoms, usage, X, codes, p, "f32")
+    trig = np.flatnonzero(codes.flags[0] & FLAG_TRIGGER)
+    assert np.all(frep[0][trig] >= 0)
+    np.testing.assert_array_equal(fc.coef[0, trig], nc.coef[0, trig])
+    np.testing.assert_array_equal(fc.relerr[0, trig], nc.relerr[0, trig])
+
+
+def test_zero_padding_is_never_selected():
+    p, hist = _append_run(steps=1)
+    atoms, usage, n0, X, codes, *_ = hist[0]
+    tight = oracle.encode(atoms[:, : int(n0[0])], X, p)
+    np.testing.assert_array_equal(tight.idx, codes.idx)
+    np.testing.assert_array_equal(tight.coef, codes.coef)
+
+
+# ---------------------------------------------------------------------------------------
 # the pages' tables
 # ---------------------------------------------------------------------------------------
 
