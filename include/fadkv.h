@@ -157,6 +157,19 @@ int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *
                 const fadkv_codes *codes, int32_t *replaced, void *workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/* Append-only growth: the contrast the abstract draws ("naive append-only strategies lead to
+ * dictionary growth", Fig. 3a), offered to measure it.  Same as fadkv_adapt except where a
+ * triggering row's new atom goes: dictionary t uses slots [0, n_atoms[t]) of its capacity N
+ * (dict->N; unused slots must hold zeros: they score 0 and are never selected), and its k-th
+ * triggering row (row order) writes round(x/||x||) to slot n_atoms[t] + k while slots remain,
+ * is re-coded onto it (flag REPLACED, replaced[m] = the slot) and leaves every existing atom
+ * untouched; rows past the capacity keep their code, commit its usage and get flag EXHAUSTED.
+ * n_atoms: device int32 [num_dicts], read and advanced in place (values clamped to [0, N]).
+ * Non-triggering rows commit usage exactly as in fadkv_adapt; tau_c is not used. */
+int fadkv_adapt_append(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                       int64_t M, const fadkv_codes *codes, int32_t *replaced, int32_t *n_atoms,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* x_hat[t][m] = sum over non-empty slots k of coef[t][m][k] * atoms[t][idx[t][m][k]],
  * written as out_dtype (fp32 accumulation; 16-bit outputs rounded to nearest even).
  * idx entries must be -1 or in [0, N). */

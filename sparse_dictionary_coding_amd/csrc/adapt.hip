@@ -1,4 +1,5 @@
-// Fixed-size dictionary adaptation (FAD-KV Figure 2) and reconstruction.
+// Fixed-size dictionary adaptation (FAD-KV Figure 2), its append-only contrast (abstract,
+// Fig. 3a: new atoms go to the next free slots and the dictionary grows) and reconstruction.
 //
 // Commit of one step, per dictionary, after every vector was encoded against the dictionary as
 // it stood at step start:
@@ -82,10 +83,13 @@ __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t *s_w) {
 }
 }  // namespace
 
+// n_atoms == nullptr: fixed size (inactive atoms are the candidates).  Otherwise append-only
+// growth: dictionary `dict` uses slots [0, n_atoms[dict]) of its capacity N, the candidates are
+// the next free slots in order, and n_atoms[dict] grows by the number handed out.
 __global__ __launch_bounds__(SEL_THREADS) void adapt_select_kernel(
     const uint32_t *__restrict__ usage, const uint8_t *__restrict__ touched, int touched_stride,
     const uint8_t *__restrict__ flags, int N, int M, uint32_t tau_c, int32_t *__restrict__ rank,
-    int32_t *__restrict__ cand, int32_t *__restrict__ ccount) {
+    int32_t *__restrict__ cand, int32_t *__restrict__ ccount, int32_t *__restrict__ n_atoms) {
   __shared__ int s_w[SEL_WAVES];
   __shared__ uint32_t s_u[SEL_WAVES];
   const int dict = blockIdx.x;
@@ -100,6 +104,19 @@ __global__ __launch_bounds__(SEL_THREADS) void adapt_select_kernel(
     const int total = block_prefix(t, s_w, prefix);
     if (m < M) rank[row0 + m] = t ? T + prefix : -1;
     T += total;
+  }
+
+  if (n_atoms) {
+    int n0 = n_atoms[dict];
+    n0 = n0 < 0 ? 0 : (n0 > N ? N : n0);
+    const int take = T < N - n0 ? T : N - n0;
+    for (int k = tid; k < take; k += SEL_THREADS) cand[row0 + k] = n0 + k;
+    __syncthreads();   // every thread has read n_atoms[dict]
+    if (tid == 0) {
+      ccount[dict] = take;
+      n_atoms[dict] = n0 + take;
+    }
+    return;
   }
 
   const uint32_t *u = usage + (size_t)dict * N;
@@ -232,7 +249,7 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
                         int N, int M, int s, float ridge_abs, float ridge_rel, uint32_t tau_c,
                         int32_t *idx, float *coef, float *relerr, uint8_t *flags,
                         int32_t *replaced, uint8_t *touched, int touched_stride, int32_t *rank,
-                        int32_t *cand, int32_t *ccount, hipStream_t stream) {
+                        int32_t *cand, int32_t *ccount, int32_t *n_atoms, hipStream_t stream) {
   const size_t G = (size_t)num_dicts * M;
   const size_t words = (size_t)num_dicts * touched_stride / 4;
   hipLaunchKernelGGL(adapt_clear_kernel, dim3((unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096)),
@@ -240,7 +257,7 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
   hipLaunchKernelGGL(adapt_mark_kernel, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, stream, idx,
                      flags, usage, touched, touched_stride, N, M, s, G);
   hipLaunchKernelGGL(adapt_select_kernel, dim3(num_dicts), dim3(SEL_THREADS), 0, stream, usage,
-                     touched, touched_stride, flags, N, M, tau_c, rank, cand, ccount);
+                     touched, touched_stride, flags, N, M, tau_c, rank, cand, ccount, n_atoms);
   uint8_t *A = static_cast<uint8_t *>(atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
   dim3 grid((unsigned)((G + 3) / 4)), block(256);

@@ -210,7 +210,36 @@ int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *
                           replaced, ws + L.touched, L.touched_stride,
                           reinterpret_cast<int32_t *>(ws + L.rank),
                           reinterpret_cast<int32_t *>(ws + L.cand),
-                          reinterpret_cast<int32_t *>(ws + L.ccount), stream) != hipSuccess)
+                          reinterpret_cast<int32_t *>(ws + L.ccount), nullptr,
+                          stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_adapt_append(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                       int64_t M, const fadkv_codes *codes, int32_t *replaced, int32_t *n_atoms,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  FADKV_TRY(check_codes(codes));
+  if (!dict->usage || !aligned(dict->usage, 4)) return FADKV_ERR_ARG;
+  if (!replaced || !aligned(replaced, 4)) return FADKV_ERR_ARG;
+  if (!n_atoms || !aligned(n_atoms, 4)) return FADKV_ERR_ARG;
+  if (M > 0 && (!X || !aligned(X, 16))) return FADKV_ERR_ARG;
+  const Layout L = layout(dict, params, M);
+  if (M > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total))
+    return FADKV_ERR_WORKSPACE;
+  if (M == 0) return FADKV_OK;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  if (fadkv::launch_adapt(dict->dtype, dict->d, dict->atoms, dict->usage, X, dict->num_dicts,
+                          dict->N, (int)M, params->s, params->ridge_abs, params->ridge_rel,
+                          params->tau_c, codes->idx, codes->coef, codes->relerr, codes->flags,
+                          replaced, ws + L.touched, L.touched_stride,
+                          reinterpret_cast<int32_t *>(ws + L.rank),
+                          reinterpret_cast<int32_t *>(ws + L.cand),
+                          reinterpret_cast<int32_t *>(ws + L.ccount), n_atoms,
+                          stream) != hipSuccess)
     return FADKV_ERR_HIP;
   return FADKV_OK;
 }

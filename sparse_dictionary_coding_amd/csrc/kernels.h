@@ -21,7 +21,7 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
                         int N, int M, int s, float ridge_abs, float ridge_rel, uint32_t tau_c,
                         int32_t *idx, float *coef, float *relerr, uint8_t *flags,
                         int32_t *replaced, uint8_t *touched, int touched_stride, int32_t *rank,
-                        int32_t *cand, int32_t *ccount, hipStream_t stream);
+                        int32_t *cand, int32_t *ccount, int32_t *n_atoms, hipStream_t stream);
 
 hipError_t launch_reconstruct(int dtype, int d, const void *atoms, const int32_t *idx,
                               const float *coef, int num_dicts, int N, int M, int s, void *out,

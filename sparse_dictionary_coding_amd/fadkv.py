@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
         h.fadkv_reconstruct.argtypes = [P(fadkv_dict), ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_void_p]
+        h.fadkv_adapt_append.restype = ctypes.c_int
+        h.fadkv_adapt_append.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p,
+                                         ctypes.c_int64, P(fadkv_codes), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
         h.fadkv_attend_workspace_bytes.restype = ctypes.c_int
         h.fadkv_attend_workspace_bytes.argtypes = [P(fadkv_dict), ctypes.c_int64, ctypes.c_int32,
                                                    P(ctypes.c_size_t)]
@@ -344,3 +349,27 @@ def fadkv_attend(atoms: torch.Tensor, layer: int, k_idx: torch.Tensor, k_coef: t
     if st != FADKV_OK:
         raise FadkvError("fadkv_attend", st)
     return out
+
+
+def fadkv_adapt_append(atoms: torch.Tensor, usage: torch.Tensor, X: torch.Tensor, codes: Codes,
+                       params: Params, n_atoms: torch.Tensor,
+                       replaced: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Append-only growth commit: atoms [num_dicts][capacity][d] with n_atoms [num_dicts]
+    (int32, advanced in place) slots in use.  Returns replaced [num_dicts][M]."""
+    dd = _dict(atoms, usage)
+    T, N, d = atoms.shape
+    _check(X, "X", atoms.dtype)
+    M = X.shape[1]
+    _check(n_atoms, "n_atoms", torch.int32, (T,))
+    if replaced is None:
+        replaced = torch.empty(T, M, dtype=torch.int32, device=atoms.device)
+    _check(replaced, "replaced", torch.int32, (T, M))
+    if workspace is None:
+        workspace = make_workspace(atoms, params, M)
+    st = lib().fadkv_adapt_append(ctypes.byref(dd), ctypes.byref(params.c()), X.data_ptr(), M,
+                                  ctypes.byref(codes.c()), replaced.data_ptr(), n_atoms.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_adapt_append", st)
+    return replaced

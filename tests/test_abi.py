@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary_calls():
     names = declared_functions()
-    for fn in ("fadkv_encode", "fadkv_adapt", "fadkv_reconstruct", "fadkv_workspace_bytes",
+    for fn in ("fadkv_encode", "fadkv_adapt", "fadkv_adapt_append", "fadkv_reconstruct",
+               "fadkv_workspace_bytes", "fadkv_attend", "fadkv_attend_workspace_bytes",
                "fadkv_status_string", "fadkv_abi_version"):
         assert fn in names
 
@@ -136,6 +137,23 @@ def test_adapt_argument_checks():
     assert adapt(_dict(), _params(), replaced=None) == -1
     assert adapt(_dict(), _params(), ws_bytes=10) == -4
     assert adapt(_dict(), _params(), M=0, X=None, ws=None, ws_bytes=0) == 0
+
+
+def test_adapt_append_argument_checks():
+    L = fadkv.lib()
+
+    def app(dd, pp, X=FAKE, M=10, replaced=FAKE, n_atoms=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return L.fadkv_adapt_append(ctypes.byref(dd), ctypes.byref(pp), X, M,
+                                    ctypes.byref(_codes()), replaced, n_atoms, ws, ws_bytes, None)
+
+    assert app(_dict(), _params(), n_atoms=None) == -1
+    assert app(_dict(), _params(), n_atoms=FAKE + 2) == -1
+    assert app(_dict(usage=None), _params()) == -1
+    assert app(_dict(), _params(), replaced=None) == -1
+    assert app(_dict(), _params(), X=FAKE + 4) == -1
+    assert app(_dict(), _params(), ws_bytes=10) == -4
+    assert app(_dict(), _params(s=0)) == -3
+    assert app(_dict(), _params(), M=0, X=None, ws=None, ws_bytes=0) == 0
 
 
 def test_reconstruct_argument_checks():

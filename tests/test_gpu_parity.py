@@ -273,6 +273,109 @@ def test_encode_adapt_multistep_parity():
 
 
 # ------------------------------------------------------------------------------------------
+# append-only growth parity
+# ------------------------------------------------------------------------------------------
+
+def _padded(A, n_atoms):
+    """Capacity-padded dictionaries: slots at and past n_atoms[t] hold zeros."""
+    A = A.clone()
+    for t, n0 in enumerate(n_atoms):
+        A[t, n0:] = 0
+    return A
+
+
+def _compare_append(A, X, U, oc, p, dtype, n_atoms):
+    op = parity.oracle_params(p)
+    na, nu, ncodes, rep, nn = oracle.append(to_f64(A), U, to_f64(X), oc, np.array(n_atoms), op,
+                                            dtype)
+    At = A.to(DEV).clone()
+    Ut = torch.from_numpy(U.astype(np.int32)).to(DEV)
+    Nt = torch.tensor(n_atoms, dtype=torch.int32, device=DEV)
+    gcodes = parity.oracle_codes_to_gpu(oc, DEV)
+    grep = fadkv.fadkv_adapt_append(At, Ut, X.to(DEV), gcodes, p, Nt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(grep.cpu().numpy(), rep)
+    np.testing.assert_array_equal(Nt.cpu().numpy(), np.minimum(nn, A.shape[1]))
+    np.testing.assert_array_equal(Ut.cpu().numpy().astype(np.int64), nu)
+    np.testing.assert_array_equal(to_f64(At), na)
+    gi, gc, ge, gf = parity.codes_to_numpy(gcodes)
+    np.testing.assert_array_equal(gi, ncodes.idx)
+    np.testing.assert_array_equal(gf, ncodes.flags & np.uint8(0xFF ^ FLAG_NEAR_TIE))
+    np.testing.assert_allclose(gc, ncodes.coef, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(ge, ncodes.relerr, rtol=1e-6, atol=1e-7)
+    return rep, nn
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_append_parity_on_oracle_codes(dtype):
+    """Append commit of the same (oracle) codes: slots handed out in row order from
+    n_atoms, new atoms, usage, rewritten codes and the new n_atoms agree exactly."""
+    _banner(f"append {dtype}")
+    A, X, p, U = _adapt_case(dtype)
+    A = _padded(A, [192])
+    oc = oracle.encode(to_f64(A), to_f64(X), parity.oracle_params(p))
+    rep, nn = _compare_append(A, X, U, oc, p, dtype, [192])
+    trig = np.flatnonzero(oc.flags[0] & FLAG_TRIGGER)
+    assert trig.size > 0
+    assert list(rep[0][trig]) == list(range(192, 192 + trig.size))
+    assert int(nn[0]) == 192 + trig.size
+
+
+def test_append_parity_capacity_exhaustion():
+    _banner("append capacity")
+    A, X, p, U = _adapt_case("f32")
+    oc = oracle.encode(to_f64(_padded(A, [192])), to_f64(X), parity.oracle_params(p))
+    trig = np.flatnonzero(oc.flags[0] & FLAG_TRIGGER)
+    assert trig.size > 2
+    # two free slots: the first two triggering rows append, the rest are exhausted
+    rep, nn = _compare_append(_padded(A, [254]), X, U, oc, p, "f32", [254])
+    assert list(np.flatnonzero(rep[0] >= 0)) == list(trig[:2]) and int(nn[0]) == 256
+    # full dictionary, and a count past the capacity (clamped to it): nothing appended
+    for n0 in (256, 300):
+        rep, _ = _compare_append(A, X, U, oc, p, "f32", [n0])
+        assert np.all(rep == -1)
+
+
+def test_encode_append_multistep_parity():
+    """Eight steps of 64 vectors on two dictionaries that start with 128 and 160 of 256 slots in
+    use: GPU encode + append and the oracle's evolve independently and agree step by step while
+    both sides agree on the supports and trigger bits."""
+    _banner("append multistep")
+    w = Workload("steps", 2, 1, 64, 256, 32, 4, "f32", 1, 64, 4, 0.0, 0.2, None, 23)
+    g = SyntheticKV(w)
+    n_start = [128, 160]
+    A0 = _padded(g.atoms(), n_start)
+    p = fadkv.Params(n=32, s=4)
+    op = parity.oracle_params(p)
+    At = A0.to(DEV).clone()
+    Ut = torch.zeros(2, 256, dtype=torch.int32, device=DEV)
+    Nt = torch.tensor(n_start, dtype=torch.int32, device=DEV)
+    Ao, Uo, No = to_f64(A0), np.zeros((2, 256), np.int64), np.array(n_start)
+    strict_steps = 0
+    for step in range(8):
+        X = g.batch(A0, step=step, support_limit=128)
+        Xt = X.to(DEV)
+        codes = fadkv.fadkv_encode(At, Xt, p)
+        torch.cuda.synchronize()
+        gpu = parity.codes_to_numpy(codes)
+        rep_enc, oc = parity.compare_encode(Ao, to_f64(X), gpu, op)
+        rep_enc.check()
+        grep = fadkv.fadkv_adapt_append(At, Ut, Xt, codes, p, Nt)
+        torch.cuda.synchronize()
+        Ao, Uo, _, orep, No = oracle.append(Ao, Uo, to_f64(X), oc, No, op, "f32")
+        if not (np.array_equal(gpu[0], oc.idx) and
+                np.array_equal(gpu[3] & FLAG_TRIGGER, oc.flags & FLAG_TRIGGER)):
+            break
+        np.testing.assert_array_equal(grep.cpu().numpy(), orep)
+        np.testing.assert_array_equal(Nt.cpu().numpy(), No)
+        np.testing.assert_array_equal(Ut.cpu().numpy(), Uo)
+        np.testing.assert_array_equal(to_f64(At), Ao)
+        strict_steps += 1
+    assert strict_steps >= 4
+    assert np.all(No > np.array(n_start))
+
+
+# ------------------------------------------------------------------------------------------
 # reconstruct
 # ------------------------------------------------------------------------------------------
 
