@@ -41,9 +41,18 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--path", default="encode", choices=["encode", "attend"],
+    ap.add_argument("--path", default="encode", choices=["encode", "attend", "growth"],
                     help="encode: the encoder hot path (default); attend: decode attention of "
-                         "one layer over the sparse codes")
+                         "one layer over the sparse codes; growth: a long run committed both "
+                         "fixed-size and append-only, with the dictionary-size trace")
+    ap.add_argument("--growth-steps", type=int, default=0,
+                    help="decode steps of the long run (--path growth; default: the workload's)")
+    ap.add_argument("--trace-out", default="", help="per-step trace as JSON (--path growth)")
+    ap.add_argument("--tau-c", type=int, default=64,
+                    help="usage threshold below which an atom is inactive (--path growth).  The "
+                         "synthetic prefill uses every atom a few times, so with the library's "
+                         "default of 1 no atom is inactive afterwards; 64 leaves about 12%% of "
+                         "them inactive")
     ap.add_argument("--tokens", type=int, default=2048, help="cached tokens per row (--path attend)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB three times (a plain "
@@ -208,6 +217,193 @@ def bench_attend(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_growth(args):
+    """The long run (prefill, then sequential decode steps whose drifted vectors move linearly
+    over the run) committed two ways from identical inputs: fixed-size adaptation (fadkv_adapt:
+    N never changes, inactive atoms are overwritten) and append-only growth (fadkv_adapt_append:
+    every triggering row adds an atom).  Each mode encodes against its own dictionary.  The
+    append-only dictionary is kept in a buffer re-sized every RELAYOUT steps to its current
+    size plus the most it can grow before the next re-size, so its encode cost follows its size
+    (the zero slots past n_atoms score 0 and are never selected).
+
+    Prints one JSON line: `value` is the fixed-size run's encoded vectors per second of GPU time
+    (encode + commit, HIP events; input generation and re-sizing are outside), and `trace` the
+    dictionary size, per-step time and code quality of both modes at evenly spaced steps."""
+    import torch
+
+    from sparse_dictionary_coding_amd import fadkv, synth
+
+    RELAYOUT = 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload if synth.WORKLOADS[args.workload].steps > 1 else "qwen4b_long_decode"
+    wd = synth.WORKLOADS[name]
+    wp = synth.WORKLOADS.get(name.replace("_decode", "_prefill"))
+    steps = args.growth_steps or wd.steps
+    every = max(1, steps // 16)
+    gd = synth.SyntheticKV(wd, device=dev)
+    A0 = gd.atoms()
+    T, N, d = A0.shape
+    p = fadkv.Params(n=wd.n, s=wd.s, tau_c=args.tau_c)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def code_stats(codes, rep):
+        f = codes.flags
+        return torch.stack([(f & fadkv.FLAG_TRIGGER).ne(0).sum().float(),
+                            rep.ge(0).sum().float(),
+                            (f & fadkv.FLAG_EXHAUSTED).ne(0).sum().float(),
+                            codes.relerr.mean()])
+
+    def clone_codes(c):
+        return fadkv.Codes(c.idx.clone(), c.coef.clone(), c.relerr.clone(), c.flags.clone())
+
+    # ---- prefill: one encode, committed both ways ----------------------------------------
+    A_fix = A0.clone()
+    U_fix = torch.zeros(T, N, dtype=torch.int32, device=dev)
+    prefill = {"vectors": 0, "ms": 0.0}
+    cap = N + RELAYOUT * wd.M
+    if wp is not None:
+        gp = synth.SyntheticKV(wp, device=dev)
+        assert torch.equal(gp.atoms(), A0), "prefill and decode draw the same dictionaries"
+        Xp = gp.batch(A0)
+        e = [ev() for _ in range(3)]
+        e[0].record(stream)
+        cp = fadkv.fadkv_encode(A0, Xp, p, stream=stream)
+        ca = clone_codes(cp)
+        e[1].record(stream)
+        rp = fadkv.fadkv_adapt(A_fix, U_fix, Xp, cp, p, stream=stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        trig_max = int((ca.flags & fadkv.FLAG_TRIGGER).ne(0).sum(1).max().item())
+        cap = N + trig_max + RELAYOUT * wd.M
+        prefill = {"vectors": T * wp.M, "ms": e[0].elapsed_time(e[2]),
+                   "encode_ms": e[0].elapsed_time(e[1]),
+                   "triggers": int((cp.flags & fadkv.FLAG_TRIGGER).ne(0).sum().item()),
+                   "replaced_fixed": int(rp.ge(0).sum().item())}
+    A_app = torch.zeros(T, cap, d, dtype=A0.dtype, device=dev)
+    A_app[:, :N] = A0
+    U_app = torch.zeros(T, cap, dtype=torch.int32, device=dev)
+    n_app = torch.full((T,), N, dtype=torch.int32, device=dev)
+    if wp is not None:
+        fadkv.fadkv_adapt_append(A_app, U_app, Xp, ca, p, n_app, stream=stream)
+        torch.cuda.synchronize()
+        prefill["inactive_after_prefill_fixed"] = float((U_fix < p.tau_c).sum(1).float().mean())
+        prefill["n_atoms_after_prefill_append"] = float(n_app.float().mean())
+        del Xp, cp, ca, rp
+        torch.cuda.empty_cache()
+
+    # ---- decode steps ---------------------------------------------------------------------
+    M = wd.M
+    cf, cA = fadkv.Codes.empty(T, M, wd.s, dev), fadkv.Codes.empty(T, M, wd.s, dev)
+    rf = torch.empty(T, M, dtype=torch.int32, device=dev)
+    ra = torch.empty(T, M, dtype=torch.int32, device=dev)
+    ws_f = fadkv.make_workspace(A_fix, p, M)
+    ws_a = fadkv.make_workspace(A_app, p, M)
+    st_f = torch.zeros(steps, 4, device=dev)
+    st_a = torch.zeros(steps, 4, device=dev)
+    n_hist = torch.zeros(steps, T, dtype=torch.int32, device=dev)
+    caps = []
+    evs = [[ev() for _ in range(4)] for _ in range(steps)]
+    inactive = {}
+    t_wall = time.perf_counter()
+    for k in range(steps):
+        X = gd.batch(A0, step=k)
+        if k % RELAYOUT == 0:
+            need = int(n_app.max().item()) + RELAYOUT * M
+            need = min(65535, -(-need // 32) * 32)
+            if need != A_app.shape[1]:
+                keep = min(need, A_app.shape[1])
+                A2 = torch.zeros(T, need, d, dtype=A0.dtype, device=dev)
+                A2[:, :keep] = A_app[:, :keep]
+                U2 = torch.zeros(T, need, dtype=torch.int32, device=dev)
+                U2[:, :keep] = U_app[:, :keep]
+                A_app, U_app = A2, U2
+                ws_a = fadkv.make_workspace(A_app, p, M)
+        caps.append(A_app.shape[1])
+        e = evs[k]
+        e[0].record(stream)
+        fadkv.fadkv_encode(A_fix, X, p, out=cf, workspace=ws_f, stream=stream)
+        fadkv.fadkv_adapt(A_fix, U_fix, X, cf, p, replaced=rf, workspace=ws_f, stream=stream)
+        e[1].record(stream)
+        e[2].record(stream)
+        fadkv.fadkv_encode(A_app, X, p, out=cA, workspace=ws_a, stream=stream)
+        fadkv.fadkv_adapt_append(A_app, U_app, X, cA, p, n_app, replaced=ra, workspace=ws_a,
+                                 stream=stream)
+        e[3].record(stream)
+        st_f[k] = code_stats(cf, rf)
+        st_a[k] = code_stats(cA, ra)
+        n_hist[k] = n_app
+        if (k + 1) % every == 0 or k + 1 == steps:
+            inactive[k] = (U_fix < p.tau_c).sum(1).float().mean()
+        if (k + 1) % 64 == 0:
+            print(f"[growth] step {k + 1}/{steps}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    assert A_fix.shape == (T, N, d)
+    ms_f = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_a = [e[2].elapsed_time(e[3]) for e in evs]
+    st_f, st_a, n_hist = st_f.cpu().tolist(), st_a.cpu().tolist(), n_hist.cpu()
+    rows = T * M
+    trace = []
+    for k in sorted(set(list(range(every - 1, steps, every)) + [steps - 1])):
+        lo = max(0, k + 1 - every)
+        win = range(lo, k + 1)
+
+        def avg(st, j):
+            return sum(st[i][j] for i in win) / len(win)
+
+        trace.append({
+            "step": k + 1,
+            "fixed": {"N": N, "inactive": round(float(inactive[k]), 1),
+                      "ms": round(sum(ms_f[i] for i in win) / len(win), 4),
+                      "trigger_frac": round(avg(st_f, 0) / rows, 4),
+                      "replaced_per_step": round(avg(st_f, 1), 1),
+                      "exhausted_frac": round(avg(st_f, 2) / rows, 4),
+                      "relerr_mean": round(avg(st_f, 3), 4)},
+            "append": {"n_atoms_mean": round(float(n_hist[k].float().mean()), 1),
+                       "n_atoms_max": int(n_hist[k].max()), "buffer_N": caps[k],
+                       "ms": round(sum(ms_a[i] for i in win) / len(win), 4),
+                       "trigger_frac": round(avg(st_a, 0) / rows, 4),
+                       "appended_per_step": round(avg(st_a, 1), 1),
+                       "exhausted_frac": round(avg(st_a, 2) / rows, 4),
+                       "relerr_mean": round(avg(st_a, 3), 4)},
+        })
+    esize = A0.element_size()
+    gpu_ms_fixed = prefill["ms"] + sum(ms_f)
+    vecs = prefill["vectors"] + steps * rows
+    final_n = n_hist[steps - 1].float()
+    res = {
+        "metric": "long run: encoded KV vectors/s, fixed-size vs append-only dictionary",
+        "value": vecs / (gpu_ms_fixed * 1e-3), "unit": "vectors/s", "n_gpus": 1,
+        "steps": steps, "warmup": 0, "ms_per_step": sum(ms_f) / steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wd.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wp.name if wp else ''} + {wd.name}", "num_dicts": T, "N": N,
+                   "n": wd.n, "s": wd.s, "d": d, "decode_vectors_per_dict": M,
+                   "prefill_vectors_per_dict": wp.M if wp else 0, "tau_c": p.tau_c,
+                   "timing": "HIP events around encode + commit; generation outside"},
+        "prefill": prefill,
+        "fixed": {"N_final": N, "dictionary_MiB": T * N * d * esize / 2**20,
+                  "decode_ms_total": sum(ms_f), "decode_vectors_per_s": steps * rows / (sum(ms_f) * 1e-3)},
+        "append": {"n_atoms_final_mean": float(final_n.mean()),
+                   "n_atoms_final_max": int(final_n.max()),
+                   "dictionary_MiB": float(final_n.sum()) * d * esize / 2**20,
+                   "decode_ms_total": sum(ms_a),
+                   "decode_vectors_per_s": steps * rows / (sum(ms_a) * 1e-3)},
+        "wall_s": t_wall,
+        "trace": trace,
+    }
+    if args.trace_out:
+        with open(args.trace_out, "w") as f:
+            json.dump({"ms_fixed": ms_f, "ms_append": ms_a, "stats_fixed": st_f,
+                       "stats_append": st_a, "n_atoms_mean": n_hist.float().mean(1).tolist(),
+                       "buffer_N": caps}, f)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -217,6 +413,9 @@ def main():
         sys.exit(2)
     if args.path == "attend":
         bench_attend(args)
+        return
+    if args.path == "growth":
+        bench_growth(args)
         return
 
     import torch

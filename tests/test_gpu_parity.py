@@ -63,6 +63,8 @@ SHAPES = [
     ("bf16", 128, 2048, 256, 16, 70, 2, True),
     ("f16", 128, 1024, 512, 32, 40, 1, True),
     ("f32", 128, 256, 64, 4, 31, 2, False),
+    ("bf16", 128, 40000, 256, 8, 64, 1, True),      # a grown dictionary
+    ("f16", 64, 65535, 128, 8, 20, 1, False),       # the largest N (uint16 pool indices)
 ]
 
 
