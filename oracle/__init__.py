@@ -4,4 +4,4 @@ from .fadkv_oracle import (OracleParams, Codes, VectorCode, encode, encode_vecto
                            adapt_dictionary, reconstruct, replay_support, round_to_storage,
                            screening_scores, candidate_pool, gm_support, pl_support,
                            ridge_system, ridge_coefficients, relative_residual,
-                           append, append_dictionary)
+                           append, append_dictionary, pool_recall)

@@ -21,6 +21,8 @@ Everything is computed in float64 from the stored values.  Where the pages leave
 open, the reading taken is stated at the function that implements it:
   * GM = greedy pursuit restricted to the pool (orthogonal-matching style, with the Table 5
     ridge system solved at every step); PL = the s largest |score| of the pool, one solve.
+    The yardstick "omp" (Fig. 1b's full-OMP atoms, Table 4's Cost 1.00) is the same greedy
+    with every atom a candidate, so it differs from GM only by the screening.
     (Table 4's cost column: (N + s*n)/(s*N) = 0.1875 and (N + s*s)/(s*N) = 0.127.)
   * scores are raw inner products <d_j, x>, ranked by absolute value; every tie goes to the
     lowest atom index;
@@ -70,7 +72,8 @@ class OracleParams:
     delta_key: float = 0.50      # even dictionaries hold keys
     delta_value: float = 0.70    # odd dictionaries hold values
     tau_c: int = 1               # inactive <=> usage < tau_c
-    select: str = "gm"           # "gm" greedy in pool, "pl" s largest of pool
+    select: str = "gm"           # "gm" greedy in pool, "pl" s largest of pool, "omp" greedy
+                                 # over the whole dictionary (the yardstick; n unused)
 
     def delta(self, dict_index: int) -> float:
         return self.delta_key if dict_index % 2 == 0 else self.delta_value
@@ -238,8 +241,14 @@ def encode_vector(D: np.ndarray, x: np.ndarray, p: OracleParams, delta: float) -
         # the zero vector is represented exactly by the empty code
         return VectorCode(idx, coef, 0.0, 0)
     sigma = screening_scores(D, x)
-    pool, near_pool = candidate_pool(sigma, p.n)
-    if p.select == "gm":
+    if p.select == "omp":
+        # Full-dictionary yardstick (Fig. 1b's "full-OMP atoms", Table 4's Cost = 1.00): the
+        # same greedy steps as GM with every atom a candidate, so the only difference from GM
+        # is the screening.  There is no pool, hence no pool boundary to be near.
+        pool, near_pool = np.arange(D.shape[0]), False
+    else:
+        pool, near_pool = candidate_pool(sigma, p.n)
+    if p.select in ("gm", "omp"):
         S, c, near_sel = gm_support(D, sigma, pool, s, p.ridge_abs, p.ridge_rel)
     elif p.select == "pl":
         S, c, near_sel = pl_support(D, sigma, pool, s, p.ridge_abs, p.ridge_rel)
@@ -481,7 +490,8 @@ def replay_support(D: np.ndarray, x: np.ndarray, S_given: Sequence[int], p: Orac
     N = sigma.shape[0]
     a = np.abs(sigma)
     order = np.lexsort((np.arange(N), -a))
-    an = a[order[p.n - 1]]
+    n_eff = N if p.select == "omp" else p.n      # the yardstick's "pool" is every atom
+    an = a[order[n_eff - 1]]
     possible = set(int(j) for j in range(N) if a[j] >= an * (1 - TIE_REL))
     sure = np.array([j for j in range(N) if a[j] > an * (1 + TIE_REL)], dtype=np.int64)
     for j in S_given:
@@ -513,6 +523,27 @@ def replay_support(D: np.ndarray, x: np.ndarray, S_given: Sequence[int], p: Orac
     c = ridge_coefficients(D[S_given], sigma[S_given], p.ridge_abs, p.ridge_rel)
     e = relative_residual(D, x, S_given, c)
     return True, "", c, e
+
+
+# ----------------------------------------------------------------------------------------
+# pool-recall diagnostic (Fig. 1b)
+# ----------------------------------------------------------------------------------------
+
+def pool_recall(pool: np.ndarray, support: np.ndarray) -> float:
+    """Share of the full-dictionary atoms that the Top-n pools hold (Fig. 1b: the screened
+    pool recalls most full-OMP atoms): sum over vectors of |S_v & P_v| / sum of |S_v|, with
+    pool [..., n] and support [..., s] index arrays over the same vectors; support slots
+    below 0 are empty and not counted.  Returns 1.0 when no vector has an atom."""
+    P = np.asarray(pool).reshape(-1, np.asarray(pool).shape[-1])
+    S = np.asarray(support).reshape(-1, np.asarray(support).shape[-1])
+    hit = total = 0
+    for pv, sv in zip(P, S):
+        members = set(int(j) for j in pv)
+        for j in sv:
+            if j >= 0:
+                total += 1
+                hit += int(int(j) in members)
+    return hit / total if total else 1.0
 
 
 def with_select(p: OracleParams, select: str) -> OracleParams:

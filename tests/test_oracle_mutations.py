@@ -77,6 +77,15 @@ MUTATIONS = {
          "    trig = (flags & FLAG_TRIGGER) != 0\n    replaced"),
     "append ignores the capacity":
         ("        if nxt < cap:\n", "        if nxt < cap + 1:\n"),
+    "yardstick screens a pool first":
+        ("        pool, near_pool = np.arange(D.shape[0]), False\n",
+         "        pool, near_pool = candidate_pool(sigma, p.n)\n"),
+    "replay bounds the yardstick by the pool size":
+        ("    n_eff = N if p.select == \"omp\" else p.n", "    n_eff = p.n"),
+    "recall counts empty slots":
+        ("            if j >= 0:\n                total += 1", "            if True:\n                total += 1"),
+    "recall against the wrong vector's pool":
+        ("    for pv, sv in zip(P, S):", "    for pv, sv in zip(P[::-1], S):"),
     "PL takes the pool head unsorted":
         ("    S = [int(j) for j in pool[order[:s]]]", "    S = [int(j) for j in pool[::-1][:s]]"),
 }

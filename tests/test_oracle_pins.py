@@ -620,3 +620,114 @@ def test_table5_defaults():
     assert (p.n, p.s) == (g["by_model_size"]["3B"]["n"], g["by_model_size"]["3B"]["s"])
     assert p.ridge_abs == g["ridge"]["abs"] and p.ridge_rel == g["ridge"]["rel_diag_G"]
     assert p.delta_key == g["delta"]["key"] and p.delta_value == g["delta"]["value"]
+
+
+# ---------------------------------------------------------------------------------------
+# full-dictionary yardstick ("omp") and the pool-recall diagnostic (Fig. 1b)
+# ---------------------------------------------------------------------------------------
+
+def test_omp_is_textbook_omp_whatever_the_pool_size():
+    """select="omp" with lambda = 0 is OMP over the whole dictionary even when n is far below
+    N: supports (as sets) and least-squares coefficients match scikit-learn's orthogonal_mp.
+    Catches a yardstick that screens a pool first."""
+    from sklearn.linear_model import orthogonal_mp
+    rng = np.random.default_rng(31)
+    checked = outside = 0
+    for trial in range(40):
+        N, d, s = 60, 20, 5
+        D = unit_rows(rng.standard_normal((N, d)))
+        x = rng.standard_normal(d)
+        p = OracleParams(n=s, s=s, ridge_abs=0.0, ridge_rel=0.0, select="omp")
+        vc = oracle.encode_vector(D, x, p, 0.5)
+        if vc.ties:
+            continue
+        ref = orthogonal_mp(D.T, x, n_nonzero_coefs=s)
+        assert set(np.flatnonzero(ref)) == set(vc.idx.tolist())
+        np.testing.assert_allclose(ref[vc.idx], vc.coef, rtol=1e-8, atol=1e-10)
+        top = set(np.argsort(-np.abs(D @ x))[:s].tolist())
+        outside += int(not set(vc.idx.tolist()) <= top)
+        checked += 1
+    assert checked >= 30 and outside >= 5
+
+
+def test_gm_equals_omp_when_the_pool_holds_every_omp_pick():
+    """If each full-dictionary greedy pick lies in the Top-n pool, GM (same ridge) makes the
+    same picks in the same order with the same coefficients; vectors where an OMP atom is
+    missing from the pool are where the two may part (and some must, at this pool size)."""
+    rng = np.random.default_rng(32)
+    N, d, s, n = 200, 32, 6, 40
+    D = unit_rows(rng.standard_normal((N, d)))
+    same = differ = 0
+    for _ in range(120):
+        x = rng.standard_normal(d)
+        po = OracleParams(n=n, s=s, select="omp")
+        pg = OracleParams(n=n, s=s, select="gm")
+        vo = oracle.encode_vector(D, x, po, 0.5)
+        vg = oracle.encode_vector(D, x, pg, 0.5)
+        if vo.ties or vg.ties:
+            continue
+        pool, _ = oracle.candidate_pool(D @ x, n)
+        if set(vo.idx.tolist()) <= set(pool.tolist()):
+            assert vo.idx.tolist() == vg.idx.tolist()
+            np.testing.assert_allclose(vo.coef, vg.coef, rtol=1e-12)
+            assert vo.relerr == pytest.approx(vg.relerr, rel=1e-12)
+            same += 1
+        else:
+            differ += 1
+            assert vo.relerr <= vg.relerr * (1 + 1e-9) or vo.idx.tolist() != vg.idx.tolist()
+    assert same >= 10 and differ >= 5
+
+
+def test_replay_accepts_own_choices_and_rejects_a_swapped_atom():
+    """replay_support validates a support chosen elsewhere: the oracle's own GM, PL and
+    yardstick supports pass, and replacing one atom by the atom of smallest |score| fails."""
+    rng = np.random.default_rng(33)
+    N, d, s, n = 80, 16, 4, 8
+    D = unit_rows(rng.standard_normal((N, d)))
+    for sel in ("gm", "pl", "omp"):
+        p = OracleParams(n=n, s=s, select=sel)
+        ok = 0
+        for _ in range(20):
+            x = rng.standard_normal(d)
+            vc = oracle.encode_vector(D, x, p, 0.5)
+            valid, why, c, e = oracle.replay_support(D, x, vc.idx, p)
+            assert valid, (sel, why)
+            np.testing.assert_allclose(c, vc.coef, rtol=1e-10)
+            worst = int(np.argmin(np.abs(D @ x)))
+            if worst in vc.idx:
+                continue
+            bad = vc.idx.copy()
+            bad[-1] = worst
+            assert not oracle.replay_support(D, x, bad, p)[0], sel
+            ok += 1
+        assert ok >= 15
+
+
+def test_pool_recall_by_hand():
+    pool = np.array([[3, 1, 7], [0, 2, 4]])
+    supp = np.array([[1, 7, 9, -1], [4, -1, -1, -1]])
+    assert oracle.pool_recall(pool, supp) == pytest.approx(3 / 4)
+    assert oracle.pool_recall(pool, -np.ones((2, 4), int)) == 1.0
+    assert oracle.pool_recall(pool[None], supp[None]) == pytest.approx(3 / 4)
+
+
+def test_pool_recall_is_one_on_planted_incoherent_vectors():
+    """Mutual coherence 1/4, planted 2-sparse vectors with coefficients +-1: a planted atom
+    scores at least 1 - 1/4 and any other at most 2/4, so the yardstick recovers the support
+    and the pool of the 2 largest |scores| is exactly it: recall 1.  A pool of 1 holds one of
+    the two atoms: recall 1/2."""
+    D = _low_coherence_dictionary()
+    rng = np.random.default_rng(34)
+    pools, pools1, supps = [], [], []
+    p = OracleParams(n=4, s=2, ridge_abs=0.0, ridge_rel=0.0, select="omp")
+    for _ in range(40):
+        S = rng.choice(D.shape[0], 2, replace=False)
+        a = rng.choice([-1.0, 1.0], 2)
+        x = a @ D[S]
+        vc = oracle.encode_vector(D, x, p, 0.5)
+        assert set(vc.idx.tolist()) == set(S.tolist())
+        pools.append(oracle.candidate_pool(D @ x, 2)[0])
+        pools1.append(oracle.candidate_pool(D @ x, 1)[0])
+        supps.append(vc.idx)
+    assert oracle.pool_recall(np.array(pools), np.array(supps)) == 1.0
+    assert oracle.pool_recall(np.array(pools1), np.array(supps)) == 0.5
