@@ -75,9 +75,9 @@ def measured_traffic(workload, select, kernel):
     if rec is None or rec.get("select") != select or kernel not in rec:
         return None
     csrc = os.path.join(ROOT, "sparse_dictionary_coding_amd", "csrc")
-    src = {"select_kernel": "select.hip", "score_topn_kernel": "score_topn.hip"}[kernel]
+    src = {"select_kernel": ("select.hip",), "score_topn_kernel": ("score_topn.hip", "tiles.h")}[kernel]
     h = hashlib.sha256()
-    for name in (src, "common.h"):
+    for name in (*src, "common.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     if h.hexdigest()[:16] != rec[kernel]["sources_sha256_16"]:

@@ -140,6 +140,20 @@ int fadkv_select_support(const fadkv_dict *dict, const fadkv_params *params, con
                          int64_t M, const uint16_t *pool_idx, const float *pool_score,
                          const uint8_t *vstatus, const fadkv_codes *out, hipStream_t stream);
 
+/* Full-dictionary greedy yardstick: the "full-OMP atoms" Figure 1b compares the screened pool
+ * against, and the Cost 1.00 reference of Table 4.  The same greedy steps as GM (largest
+ * |rho_j| = |<d_j, x - D_S^T c>|, ties to the lowest index, chosen atoms excluded, the ridge
+ * system of Table 5 re-solved at every step) with every atom of the dictionary a candidate
+ * instead of the Top-n pool; params->n and params->select are not used.  Writes `out` as
+ * fadkv_encode does (same zero and non-finite handling, same trigger against delta).
+ * Launches 1 + 2 s kernels on `stream`.  workspace: fadkv_omp_workspace_bytes(), 256-byte
+ * aligned, owned by the caller; X: device [num_dicts][M][d], 16-byte aligned. */
+int fadkv_omp_workspace_bytes(const fadkv_dict *dict, const fadkv_params *params, int64_t M,
+                              size_t *bytes);
+int fadkv_encode_omp(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                     int64_t M, const fadkv_codes *out, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
 /* Commit one step's codes and apply fixed-size adaptation (Figure 2), per dictionary:
  *   1. usage[j] += 1 for every atom of every non-triggering code;
  *   2. candidates = atoms with usage < tau_c that no code of this step selected, ordered by

@@ -88,6 +88,25 @@ size_t attend_ws_bytes(const fadkv_dict *dict, int64_t R, int32_t G) {
   return align_up(RG * (size_t)dict->N * sizeof(float) + ranges * RG * (size_t)dict->d * sizeof(float));
 }
 
+struct OmpLayout {
+  size_t status, jstar, S, L, sig, R, total;
+};
+
+OmpLayout omp_layout(const fadkv_dict *dict, const fadkv_params *p, int64_t M) {
+  OmpLayout L{};
+  const size_t G = (size_t)dict->num_dicts * (size_t)M;
+  const size_t s = (size_t)p->s;
+  size_t o = 0;
+  L.status = o; o = align_up(o + G);
+  L.jstar = o;  o = align_up(o + G * sizeof(int32_t));
+  L.S = o;      o = align_up(o + G * s * sizeof(int32_t));
+  L.L = o;      o = align_up(o + G * s * s * sizeof(float));
+  L.sig = o;    o = align_up(o + G * s * sizeof(float));
+  L.R = o;      o = align_up(o + G * fadkv::omp_residual_row_bytes(dict->dtype, dict->d));
+  L.total = o;
+  return L;
+}
+
 #define FADKV_TRY(expr)        \
   do {                         \
     const int _st = (expr);    \
@@ -213,6 +232,57 @@ int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *
                           reinterpret_cast<int32_t *>(ws + L.ccount), nullptr,
                           stream) != hipSuccess)
     return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_omp_workspace_bytes(const fadkv_dict *dict, const fadkv_params *params, int64_t M,
+                              size_t *bytes) {
+  if (!bytes || !dict) return FADKV_ERR_ARG;
+  if (dict->dtype != FADKV_F32 && dict->dtype != FADKV_F16 && dict->dtype != FADKV_BF16)
+    return FADKV_ERR_DTYPE;
+  if (dict->num_dicts < 1 || dict->N < 1 || dict->N > kMaxN || (dict->d != 64 && dict->d != 128))
+    return FADKV_ERR_SHAPE;
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  *bytes = omp_layout(dict, params, M).total;
+  return FADKV_OK;
+}
+
+int fadkv_encode_omp(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                     int64_t M, const fadkv_codes *out, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  FADKV_TRY(check_codes(out));
+  if (M > 0 && (!X || !aligned(X, 16))) return FADKV_ERR_ARG;
+  const OmpLayout L = omp_layout(dict, params, M);
+  if (M > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total))
+    return FADKV_ERR_WORKSPACE;
+  if (M == 0) return FADKV_OK;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  fadkv::OmpArgs a{};
+  a.atoms = dict->atoms;
+  a.X = X;
+  a.num_dicts = dict->num_dicts;
+  a.N = dict->N;
+  a.M = (int)M;
+  a.s = params->s;
+  a.ridge_abs = params->ridge_abs;
+  a.ridge_rel = params->ridge_rel;
+  a.delta_key = params->delta_key;
+  a.delta_value = params->delta_value;
+  a.status = ws + L.status;
+  a.jstar = reinterpret_cast<int32_t *>(ws + L.jstar);
+  a.S = reinterpret_cast<int32_t *>(ws + L.S);
+  a.L = reinterpret_cast<float *>(ws + L.L);
+  a.sig = reinterpret_cast<float *>(ws + L.sig);
+  a.R = ws + L.R;
+  a.idx = out->idx;
+  a.coef = out->coef;
+  a.relerr = out->relerr;
+  a.flags = out->flags;
+  if (fadkv::launch_omp(dict->dtype, dict->d, a, stream) != hipSuccess) return FADKV_ERR_HIP;
   return FADKV_OK;
 }
 

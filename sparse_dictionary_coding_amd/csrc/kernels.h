@@ -34,4 +34,24 @@ hipError_t launch_attend(int dtype, int d, const void *dictK, const void *dictV,
                          const float *v_coef, const int32_t *lens, int R, int T, const void *q,
                          int G, float scale, float *out, float *ws, hipStream_t stream);
 
+// full-dictionary greedy yardstick: init, then per step a correlation sweep and an update
+struct OmpArgs {
+  const void *atoms;
+  const void *X;
+  int num_dicts, N, M, s;
+  float ridge_abs, ridge_rel, delta_key, delta_value;
+  uint8_t *status;   // [G] vector class
+  int32_t *jstar;    // [G] atom chosen by the current step
+  int32_t *S;        // [G][s] chosen atoms, selection order
+  float *L;          // [G][s][s] Cholesky rows
+  float *sig;        // [G][s] <d_S[i], x>
+  uint8_t *R;        // [G] residual rows (omp_residual_row_bytes each)
+  int32_t *idx;
+  float *coef;
+  float *relerr;
+  uint8_t *flags;
+};
+size_t omp_residual_row_bytes(int dtype, int d);
+hipError_t launch_omp(int dtype, int d, const OmpArgs &a, hipStream_t stream);
+
 }  // namespace fadkv

@@ -92,6 +92,13 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int64, P(fadkv_codes), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]
+        h.fadkv_omp_workspace_bytes.restype = ctypes.c_int
+        h.fadkv_omp_workspace_bytes.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_int64,
+                                                P(ctypes.c_size_t)]
+        h.fadkv_encode_omp.restype = ctypes.c_int
+        h.fadkv_encode_omp.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p,
+                                       ctypes.c_int64, P(fadkv_codes), ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
         h.fadkv_attend_workspace_bytes.restype = ctypes.c_int
         h.fadkv_attend_workspace_bytes.argtypes = [P(fadkv_dict), ctypes.c_int64, ctypes.c_int32,
                                                    P(ctypes.c_size_t)]
@@ -373,3 +380,35 @@ def fadkv_adapt_append(atoms: torch.Tensor, usage: torch.Tensor, X: torch.Tensor
     if st != FADKV_OK:
         raise FadkvError("fadkv_adapt_append", st)
     return replaced
+
+
+def fadkv_omp_workspace_bytes(atoms: torch.Tensor, params: Params, M: int) -> int:
+    T, N, d = atoms.shape
+    dd = fadkv_dict(T, N, d, _DT[atoms.dtype], None, None)
+    out = ctypes.c_size_t(0)
+    st = lib().fadkv_omp_workspace_bytes(ctypes.byref(dd), ctypes.byref(params.c()), int(M),
+                                         ctypes.byref(out))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_omp_workspace_bytes", st)
+    return out.value
+
+
+def fadkv_encode_omp(atoms: torch.Tensor, X: torch.Tensor, params: Params,
+                     out: Optional[Codes] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Codes:
+    """Full-dictionary greedy yardstick (every atom a candidate); codes as fadkv_encode."""
+    dd = _dict(atoms, None)
+    T, N, d = atoms.shape
+    _check(X, "X", atoms.dtype)
+    M = X.shape[1]
+    if out is None:
+        out = Codes.empty(T, M, params.s, atoms.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, fadkv_omp_workspace_bytes(atoms, params, M)),
+                                dtype=torch.uint8, device=atoms.device)
+    st = lib().fadkv_encode_omp(ctypes.byref(dd), ctypes.byref(params.c()), X.data_ptr(), M,
+                                ctypes.byref(out.c()), workspace.data_ptr(), workspace.numel(),
+                                _stream(stream))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_encode_omp", st)
+    return out

@@ -156,6 +156,32 @@ def test_adapt_append_argument_checks():
     assert app(_dict(), _params(), M=0, X=None, ws=None, ws_bytes=0) == 0
 
 
+def test_encode_omp_argument_checks():
+    L = fadkv.lib()
+
+    def omp(dd, pp, X=FAKE, M=10, ws=FAKE, ws_bytes=1 << 40, codes=None):
+        c = _codes() if codes is None else codes
+        return L.fadkv_encode_omp(ctypes.byref(dd), ctypes.byref(pp), X, M, ctypes.byref(c), ws,
+                                  ws_bytes, None)
+
+    assert omp(_dict(), _params(), X=None) == -1
+    assert omp(_dict(), _params(), X=FAKE + 8) == -1
+    assert omp(_dict(dtype=7), _params()) == -2
+    assert omp(_dict(d=96), _params()) == -3
+    assert omp(_dict(N=4), _params(n=8, s=8)) == -3        # s <= n <= N
+    assert omp(_dict(), _params(s=33)) == -3
+    assert omp(_dict(), _params(), ws_bytes=100) == -4
+    assert omp(_dict(), _params(), ws=FAKE + 64) == -4
+    assert omp(_dict(), _params(), M=-1) == -1
+    assert omp(_dict(), _params(), M=0, X=None, ws=None, ws_bytes=0) == 0
+    out = ctypes.c_size_t(0)
+    assert L.fadkv_omp_workspace_bytes(ctypes.byref(_dict(num_dicts=56, N=4096)),
+                                       ctypes.byref(_params()), 256, ctypes.byref(out)) == 0
+    G = 56 * 256
+    assert out.value >= G * (1 + 4 + 8 * 4 + 64 * 4 + 8 * 4 + 2 * 128 * 2)
+    assert out.value % 256 == 0
+
+
 def test_reconstruct_argument_checks():
     L = fadkv.lib()
 

@@ -1,6 +1,6 @@
 """Checks on the generated gfx950 code that the kernels' correctness relies on (CPU only).
 
-The screening kernel writes M0 in inline assembly to drive its global -> LDS copies; that is
+The screening kernel and the yardstick's correlation sweep write M0 in inline assembly to drive its global -> LDS copies; that is
 only sound while the compiler itself keeps nothing in M0 in these kernels.  The test compiles
 the source to assembly and requires every M0 access to be one of those copies.
 """
@@ -17,9 +17,10 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-def test_m0_written_only_by_lds_copies(tmp_path):
-    src = os.path.join(build.CSRC, "score_topn.hip")
-    out = tmp_path / "score_topn.s"
+@pytest.mark.parametrize("name", ["score_topn.hip", "omp.hip"])
+def test_m0_written_only_by_lds_copies(tmp_path, name):
+    src = os.path.join(build.CSRC, name)
+    out = tmp_path / (name + ".s")
     cmd = [HIPCC, *build.HIPCC_FLAGS, f"-I{build.INCLUDE}", f"-I{build.CSRC}",
            "--cuda-device-only", "-S", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
