@@ -41,10 +41,12 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--path", default="encode", choices=["encode", "attend", "growth"],
+    ap.add_argument("--path", default="encode", choices=["encode", "attend", "growth", "omp"],
                     help="encode: the encoder hot path (default); attend: decode attention of "
                          "one layer over the sparse codes; growth: a long run committed both "
-                         "fixed-size and append-only, with the dictionary-size trace")
+                         "fixed-size and append-only, with the dictionary-size trace; omp: "
+                         "coding cost of GM and PL relative to the full-dictionary greedy "
+                         "yardstick, and the pool recall of the yardstick's atoms")
     ap.add_argument("--growth-steps", type=int, default=0,
                     help="decode steps of the long run (--path growth; default: the workload's)")
     ap.add_argument("--trace-out", default="", help="per-step trace as JSON (--path growth)")
@@ -404,6 +406,108 @@ def bench_growth(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_omp(args):
+    """Table 4's Cost column measured: the time of the screening encoder (GM, PL) relative to
+    the full-dictionary greedy yardstick on the same step, plus Fig. 1b's pool recall (share of
+    the yardstick's atoms inside the Top-n pool, over every vector of the step, for several n).
+    Same cold-dictionary protocol as the main path.  Prints one JSON line whose `value` is the
+    GM/yardstick time ratio (lower is better)."""
+    import numpy as np
+    import torch
+
+    from sparse_dictionary_coding_amd import fadkv, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    T, M, N, d = w.num_dicts, w.M, w.N, w.d
+    esize = 2 if w.dtype != "f32" else 4
+    dict_bytes = T * N * d * esize
+    R = 1 if args.warm else min(8, max(1, -(-(MALL_BYTES + (MALL_BYTES >> 2)) // dict_bytes)))
+    gen = synth.SyntheticKV(w, device=dev)
+    base = gen.atoms()
+    sets = [base.clone() for _ in range(R)]
+    X = gen.batch(base)
+    pg, pp = fadkv.Params(n=w.n, s=w.s, select="gm"), fadkv.Params(n=w.n, s=w.s, select="pl")
+    ws = fadkv.make_workspace(base, pg, M)
+    ws_omp = torch.empty(fadkv.fadkv_omp_workspace_bytes(base, pg, M), dtype=torch.uint8,
+                         device=dev)
+    cg, cp, co = (fadkv.Codes.empty(T, M, w.s, dev) for _ in range(3))
+    stream = torch.cuda.current_stream()
+    runs = {
+        "gm": lambda A: fadkv.fadkv_encode(A, X, pg, out=cg, workspace=ws, stream=stream),
+        "pl": lambda A: fadkv.fadkv_encode(A, X, pp, out=cp, workspace=ws, stream=stream),
+        "omp": lambda A: fadkv.fadkv_encode_omp(A, X, pg, out=co, workspace=ws_omp, stream=stream),
+    }
+    ms = {}
+    for name, fn in runs.items():
+        for k in range(args.warmup):
+            fn(sets[k % R])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(ev):
+            a.record(stream)
+            fn(sets[(args.warmup + k) % R])
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms[name] = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    G = T * M
+    # pool recall of the yardstick's atoms, over every vector of the step
+    oi = co.idx.to(torch.int64)
+    recall = {}
+    for n in sorted({32, 64, 128, w.n, min(2 * w.n, 512)}):
+        if n < w.s or n > min(N, 512):
+            continue
+        pool = fadkv.fadkv_screen(base, X, fadkv.Params(n=n, s=w.s))
+        P = pool.atom_indices()
+        hit = torch.zeros((), dtype=torch.int64, device=dev)
+        for t0 in range(0, T, 8):
+            sl = slice(t0, t0 + 8)
+            hit += ((oi[sl, :, :, None] == P[sl, :, None, :]).any(-1) & (oi[sl] >= 0)).sum()
+        recall[n] = float(hit) / float((oi >= 0).sum())
+    same_support = float((torch.sort(cg.idx, -1).values == torch.sort(co.idx, -1).values)
+                         .all(-1).float().mean())
+    ratio_gm, ratio_pl = ms["gm"] / ms["omp"], ms["pl"] / ms["omp"]
+    flops = 2.0 * N * d * w.s * G        # s correlation passes over the whole dictionary
+    ach = flops / (ms["omp"] * 1e-3) / 1e12
+    res = {
+        "metric": "sparse-coding cost relative to the full-dictionary greedy (Table 4 Cost)",
+        "value": ratio_gm, "unit": "GM time / full-dictionary time", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms["gm"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": ratio_gm / 0.19,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_dicts": T, "vectors_per_dict": M, "N": N, "n": w.n,
+                   "s": w.s, "d": d, "dictionary_sets": R},
+        "ms": {k: round(v, 5) for k, v in ms.items()},
+        "cost_ratio": {"gm": ratio_gm, "pl": ratio_pl, "pages_gm": 0.19, "pages_pl": 0.13},
+        "pool_recall": recall,
+        "gm_equals_full_support_frac": same_support,
+        "mean_relerr": {"gm": float(cg.relerr.nan_to_num().mean()),
+                        "pl": float(cp.relerr.nan_to_num().mean()),
+                        "omp": float(co.relerr.nan_to_num().mean())},
+        "roofline": {"kernel": "fadkv_encode_omp (all launches)", "bound": "mfma",
+                     "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        A = synth.to_f64(base[:1])
+        Xs = synth.to_f64(X[:1])
+        op = oracle.OracleParams(n=w.n, s=w.s, select="omp",
+                                 ridge_abs=float(np.float32(1e-4)), ridge_rel=float(np.float32(0.2)))
+        t1 = time.perf_counter()
+        rows = 0
+        while time.perf_counter() - t1 < args.cpu_seconds and rows < M:
+            oracle.encode_vector(A[0], Xs[0, rows], op, op.delta(0))
+            rows += 1
+        dt = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": rows / dt, "unit": "vectors/s (full-dictionary greedy)",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} vectors of dictionary 0 (NumPy fp64), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -416,6 +520,9 @@ def main():
         return
     if args.path == "growth":
         bench_growth(args)
+        return
+    if args.path == "omp":
+        bench_omp(args)
         return
 
     import torch
