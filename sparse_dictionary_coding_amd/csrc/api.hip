@@ -107,6 +107,21 @@ OmpLayout omp_layout(const fadkv_dict *dict, const fadkv_params *p, int64_t M) {
   return L;
 }
 
+// the support/coefficient stage of the chosen selection mode
+hipError_t run_select(const fadkv_dict *dict, const fadkv_params *p, const void *X, int64_t M,
+                      const uint16_t *pool_idx, const float *pool_sig, const uint8_t *vstat,
+                      const fadkv_codes *out, hipStream_t stream) {
+  if (p->select == FADKV_SELECT_PL)
+    return fadkv::launch_select_pl(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N,
+                                   (int)M, p->n, p->s, p->ridge_abs, p->ridge_rel, p->delta_key,
+                                   p->delta_value, pool_idx, pool_sig, vstat, out->idx, out->coef,
+                                   out->relerr, out->flags, stream);
+  return fadkv::launch_select(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N,
+                              (int)M, p->n, p->s, p->ridge_abs, p->ridge_rel, p->delta_key,
+                              p->delta_value, pool_idx, pool_sig, vstat, out->idx, out->coef,
+                              out->relerr, out->flags, stream);
+}
+
 #define FADKV_TRY(expr)        \
   do {                         \
     const int _st = (expr);    \
@@ -164,11 +179,7 @@ int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void 
   if (fadkv::launch_score_topn(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N,
                                (int)M, params->n, pool_idx, pool_sig, vstat, stream) != hipSuccess)
     return FADKV_ERR_HIP;
-  if (fadkv::launch_select(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N, (int)M,
-                           params->n, params->s, params->select, params->ridge_abs,
-                           params->ridge_rel, params->delta_key, params->delta_value, pool_idx,
-                           pool_sig, vstat, out->idx, out->coef, out->relerr, out->flags,
-                           stream) != hipSuccess)
+  if (run_select(dict, params, X, M, pool_idx, pool_sig, vstat, out, stream) != hipSuccess)
     return FADKV_ERR_HIP;
   return FADKV_OK;
 }
@@ -199,11 +210,7 @@ int fadkv_select_support(const fadkv_dict *dict, const fadkv_params *params, con
   if (!X || !aligned(X, 16)) return FADKV_ERR_ARG;
   if (!pool_idx || !pool_score || !vstatus || !aligned(pool_idx, 2) || !aligned(pool_score, 4))
     return FADKV_ERR_ARG;
-  if (fadkv::launch_select(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N, (int)M,
-                           params->n, params->s, params->select, params->ridge_abs,
-                           params->ridge_rel, params->delta_key, params->delta_value, pool_idx,
-                           pool_score, vstatus, out->idx, out->coef, out->relerr, out->flags,
-                           stream) != hipSuccess)
+  if (run_select(dict, params, X, M, pool_idx, pool_score, vstatus, out, stream) != hipSuccess)
     return FADKV_ERR_HIP;
   return FADKV_OK;
 }

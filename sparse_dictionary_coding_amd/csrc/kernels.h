@@ -11,11 +11,19 @@ hipError_t launch_score_topn(int dtype, int d, const void *atoms, const void *X,
                              int N, int M, int n, uint16_t *pool_idx, float *pool_sig,
                              uint8_t *vstat, hipStream_t stream);
 
+// GM: greedy pursuit inside the pool (one workgroup per vector)
 hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int num_dicts, int N,
-                         int M, int n, int s, int select, float ridge_abs, float ridge_rel,
+                         int M, int n, int s, float ridge_abs, float ridge_rel,
                          float delta_key, float delta_value, const uint16_t *pool_idx,
                          const float *pool_sig, const uint8_t *vstat, int32_t *idx, float *coef,
                          float *relerr, uint8_t *flags, hipStream_t stream);
+
+// PL: the s largest |sigma| of the pool, one solve (one wave per vector)
+hipError_t launch_select_pl(int dtype, int d, const void *atoms, const void *X, int num_dicts,
+                            int N, int M, int n, int s, float ridge_abs, float ridge_rel,
+                            float delta_key, float delta_value, const uint16_t *pool_idx,
+                            const float *pool_sig, const uint8_t *vstat, int32_t *idx,
+                            float *coef, float *relerr, uint8_t *flags, hipStream_t stream);
 
 hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const void *X, int num_dicts,
                         int N, int M, int s, float ridge_abs, float ridge_rel, uint32_t tau_c,

@@ -14,8 +14,8 @@
 //   W_{:,k} = (G_{P,j*} - W_{:,0..k-1} l) / L_kk,     rho -= W_{:,k} y_k
 // which needs one pool-wide column G_{P,j*} = D_P d_j* per step (skipped after the last
 // step) and O(k) work per pool atom.  At the end c = L^{-T} y by back substitution.
-// PL takes the s largest |sigma| of the pool the same way (no rho update) and solves once.
-// Finally r = x - D_S^T c is formed from the chosen rows and e = ||r|| / ||x||.
+// Finally r = x - D_S^T c is formed from the chosen rows and e = ||r|| / ||x||.  (PL, which
+// needs no pool rows, has its own one-wave kernel in select_pl.hip.)
 //
 // One workgroup barrier per step.  Before it, every wave reduces its own argmax (DPP) and its
 // candidate lane publishes a 64-bit key (|rho| bits, 0xFFFF - atom, wave) together with its
@@ -81,7 +81,7 @@ template <int DT> __device__ __forceinline__ float lds_elem(const uint32_t *row,
 template <int DT, int D, int SMAX, int MAXW>
 __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) void select_kernel(
     const uint8_t *__restrict__ atoms, const uint8_t *__restrict__ X, int num_dicts, int N, int M,
-    int n, int s, int select, float ridge_abs, float ridge_rel, float delta_key, float delta_value,
+    int n, int s, float ridge_abs, float ridge_rel, float delta_key, float delta_value,
     const uint16_t *__restrict__ pool_idx, const float *__restrict__ pool_sig,
     const uint8_t *__restrict__ vstat, int32_t *__restrict__ out_idx, float *__restrict__ out_coef,
     float *__restrict__ out_relerr, uint8_t *__restrict__ out_flags) {
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
   constexpr int PUB = SMAX + 2;   // published slot: W row, score, squared norm
   __shared__ __attribute__((aligned(16))) uint32_t s_selrow[SMAX][NW];  // chosen rows
   __shared__ float s_L[SMAX * SMAX];   // row k: l of step k (strictly lower part of L)
-  __shared__ float s_linv[SMAX], s_y[SMAX], s_sig[SMAX], s_c[SMAX];
+  __shared__ float s_linv[SMAX], s_y[SMAX];
   __shared__ int s_sel[SMAX];
   __shared__ unsigned long long s_key[2][MAXW];
   __shared__ float s_pub[2][MAXW][PUB];
@@ -159,7 +159,6 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
     if (D > 64) x1 = elem_f<DT>(xr, lane + 64);
   }
 
-  const bool gm = select == 0;
   float rho = sig;
   float W[SMAX], Y[SMAX];   // Y: y, the same in every lane
 #pragma unroll
@@ -217,7 +216,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
       // G_{j,j*} for this thread's row: the winning row comes through the scalar cache while
       // the published slot is read
       float acc = 0.f;
-      if (gm && k + 1 < s)
+      if (k + 1 < s)
         acc = row_dot_uniform<DT, NW>(w, reinterpret_cast<const uint32_t *>(dict_atoms + (size_t)jstar * ROWB));
       if (win) {
 #pragma unroll
@@ -225,7 +224,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
           reinterpret_cast<uint4 *>(s_selrow[k])[q] =
               make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
       }
-      if (gm) {
+      {
         float nl2 = 0.f, ly = 0.f;
 #pragma unroll
         for (int m = 0; m < k; ++m) {
@@ -250,10 +249,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
           s_y[k] = yk;
         }
       }
-      if (tid == 0) {
-        s_sel[k] = jstar;
-        s_sig[k] = sigk;
-      }
+      if (tid == 0) s_sel[k] = jstar;
     }
   }
   __syncthreads();
@@ -261,7 +257,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
 
   // ---- one wave: coefficients, residual, outputs ----
   float c = 0.f;   // lane k < s holds c_k
-  if (gm) {
+  {
     // c = L^{-T} y: lane m carries t_m = y_m - sum_{i > m} L_im c_i; column i is finished
     // once every later column has been folded in, so c_i = t_i / L_ii is final at step i
     float t = lane < s ? s_y[lane < SMAX ? lane : 0] : 0.f;
@@ -276,46 +272,6 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
       }
     }
     c = lane < s ? t * s_linv[lane < SMAX ? lane : 0] : 0.f;
-  } else {
-    // PL: G_SS from the chosen rows, then Cholesky and two triangular solves on lane 0
-    for (int e = lane; e < s * s; e += 64) {
-      const int r = e / s, cc = e % s;
-      if (cc > r) continue;
-      float acc = 0.f;
-      for (int q = 0; q < NW; ++q) {
-        const uint32_t a = s_selrow[r][q], b = s_selrow[cc][q];
-        if constexpr (DT == DT_F32) acc = fmaf(__uint_as_float(a), __uint_as_float(b), acc);
-        else acc = dot2<DT>(a, b, acc);
-      }
-      s_L[r * SMAX + cc] = acc;   // lower triangle of G_SS, factored in place below
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    if (lane == 0) {
-      for (int r = 0; r < s; ++r) s_L[r * SMAX + r] = fmaf(s_L[r * SMAX + r], 1.f + ridge_rel, ridge_abs);
-      for (int cc = 0; cc < s; ++cc) {
-        float dcc = s_L[cc * SMAX + cc];
-        for (int m = 0; m < cc; ++m) dcc = fmaf(-s_L[cc * SMAX + m], s_L[cc * SMAX + m], dcc);
-        const float Lcc = sqrtf(fmaxf(dcc, 1e-30f));
-        s_L[cc * SMAX + cc] = Lcc;
-        for (int r = cc + 1; r < s; ++r) {
-          float v = s_L[r * SMAX + cc];
-          for (int m = 0; m < cc; ++m) v = fmaf(-s_L[r * SMAX + m], s_L[cc * SMAX + m], v);
-          s_L[r * SMAX + cc] = v / Lcc;
-        }
-      }
-      for (int i = 0; i < s; ++i) {
-        float acc = s_sig[i];
-        for (int m = 0; m < i; ++m) acc = fmaf(-s_L[i * SMAX + m], s_y[m], acc);
-        s_y[i] = acc / s_L[i * SMAX + i];
-      }
-      for (int i = s - 1; i >= 0; --i) {
-        float acc = s_y[i];
-        for (int m = i + 1; m < s; ++m) acc = fmaf(-s_L[m * SMAX + i], s_c[m], acc);
-        s_c[i] = acc / s_L[i * SMAX + i];
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    c = lane < s ? s_c[lane < SMAX ? lane : 0] : 0.f;
   }
 
   // residual r = x - D_S^T c from the chosen rows; lane i holds elements i and i + 64
@@ -343,7 +299,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
 
 #define FADKV_SEL_INST(DT, D, SM, MW)                                                             \
   template __global__ void select_kernel<DT, D, SM, MW>(                                         \
-      const uint8_t *, const uint8_t *, int, int, int, int, int, int, float, float, float, float, \
+      const uint8_t *, const uint8_t *, int, int, int, int, int, float, float, float, float,      \
       const uint16_t *, const float *, const uint8_t *, int32_t *, float *, float *, uint8_t *);
 #define FADKV_SEL_INST_S(DT, D, SM) FADKV_SEL_INST(DT, D, SM, 4) FADKV_SEL_INST(DT, D, SM, 8)
 #define FADKV_SEL_INST_D(DT, D) \
@@ -356,7 +312,7 @@ FADKV_SEL_INST_D(DT_BF16, 64)
 FADKV_SEL_INST_D(DT_BF16, 128)
 
 hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int num_dicts, int N,
-                         int M, int n, int s, int select, float ridge_abs, float ridge_rel,
+                         int M, int n, int s, float ridge_abs, float ridge_rel,
                          float delta_key, float delta_value, const uint16_t *pool_idx,
                          const float *pool_sig, const uint8_t *vstat, int32_t *idx, float *coef,
                          float *relerr, uint8_t *flags, hipStream_t stream) {
@@ -367,7 +323,7 @@ hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
 #define L(DT, D, SM, MW)                                                                          \
   hipLaunchKernelGGL((select_kernel<DT, D, SM, MW>), grid, block, 0, stream, A, Xb, num_dicts, N, \
-                     M, n, s, select, ridge_abs, ridge_rel, delta_key, delta_value, pool_idx,      \
+                     M, n, s, ridge_abs, ridge_rel, delta_key, delta_value, pool_idx,              \
                      pool_sig, vstat, idx, coef, relerr, flags)
 #define LW(DT, D, SM) do { if (threads <= 256) L(DT, D, SM, 4); else L(DT, D, SM, 8); } while (0)
 #define LS(DT, D) \
