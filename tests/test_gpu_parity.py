@@ -411,13 +411,13 @@ def _sample_rows(T, M, count, seed):
     return sorted(set(zip(ts.tolist(), ms.tolist())))
 
 
-def _full_size(name, samples, steps=1):
+def _full_size(name, samples, steps=1, select="gm"):
     w = synth.WORKLOADS[name]
-    _banner(f"full size {name}: {w.num_dicts} dicts x {w.M} vectors")
+    _banner(f"full size {name} ({select}): {w.num_dicts} dicts x {w.M} vectors")
     g = SyntheticKV(w, device=DEV)
     A = g.atoms()
     U = torch.zeros(w.num_dicts, w.N, dtype=torch.int32, device=DEV)
-    p = fadkv.Params(n=w.n, s=w.s)
+    p = fadkv.Params(n=w.n, s=w.s, select=select)
     ws = fadkv.make_workspace(A, p, w.M)
     op = parity.oracle_params(p)
     for step in range(steps):
@@ -469,3 +469,11 @@ def test_full_size_llama3b_prefill_sampled():
 
 def test_full_size_qwen4b_decode_sampled():
     _full_size("qwen4b_long_decode", samples=64, steps=2)
+
+
+def test_full_size_llama3b_decode_pl_sampled():
+    _full_size("llama3b_decode", samples=96, steps=2, select="pl")
+
+
+def test_full_size_llama8b_decode_pl_sampled():
+    _full_size("llama8b_decode", samples=48, select="pl")
