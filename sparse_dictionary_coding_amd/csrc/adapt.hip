@@ -144,6 +144,53 @@ __global__ __launch_bounds__(SEL_THREADS) void adapt_select_kernel(
   if (tid == 0) ccount[dict] = count < T ? count : T;
 }
 
+// The replacement of one triggering row by one wave: the atom row becomes x/||x|| (fp64,
+// rounded to the storage dtype) and the row's code the single new atom with the one-atom ridge
+// coefficient c = <a, x> / ((1 + ridge_rel) <a, a> + ridge_abs); e = ||x - c a|| / ||x||.
+template <int DT, int D>
+__device__ __forceinline__ void recode_onto_new_atom(uint8_t *__restrict__ arow,
+                                                     const uint8_t *__restrict__ xr,
+                                                     float ridge_abs, float ridge_rel, int lane,
+                                                     float &c_out, float &e_out) {
+  constexpr int PER = D / 64;   // elements per lane
+  double x[PER];
+  double ss = 0.0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    x[p] = (double)elem_f<DT>(xr, lane + 64 * p);
+    ss += x[p] * x[p];
+  }
+  const double nrm = __builtin_sqrt(wave_sum_d(ss));
+  double a[PER];
+  double g = 0.0, ax = 0.0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = lane + 64 * p;
+    const uint32_t bits = double_to_storage_bits<DT>(x[p] / nrm);
+    if constexpr (DT == DT_F32) {
+      reinterpret_cast<uint32_t *>(arow)[i] = bits;
+      a[p] = (double)__uint_as_float(bits);
+    } else {
+      reinterpret_cast<uint16_t *>(arow)[i] = (uint16_t)bits;
+      a[p] = (double)(DT == DT_F16 ? f16_bits_to_float(bits) : bf16_bits_to_float(bits));
+    }
+    g += a[p] * a[p];
+    ax += a[p] * x[p];
+  }
+  g = wave_sum_d(g);
+  ax = wave_sum_d(ax);
+  const double c = ax / ((1.0 + (double)ridge_rel) * g + (double)ridge_abs);
+  double rr = 0.0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const double d = x[p] - c * a[p];
+    rr += d * d;
+  }
+  rr = wave_sum_d(rr);
+  c_out = (float)c;
+  e_out = (float)(__builtin_sqrt(rr) / nrm);
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) void adapt_apply_kernel(
     uint8_t *__restrict__ atoms, uint32_t *__restrict__ usage, const uint8_t *__restrict__ X, int N,
@@ -152,7 +199,6 @@ __global__ __launch_bounds__(256) void adapt_apply_kernel(
     float *__restrict__ coef, float *__restrict__ relerr, uint8_t *__restrict__ flags,
     int32_t *__restrict__ replaced, size_t G) {
   constexpr int ROWB = D * Elem<DT>::bytes;
-  constexpr int PER = D / 64;   // elements per lane
   const int lane = threadIdx.x & 63;
   const size_t gv = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gv >= G) return;
@@ -164,49 +210,16 @@ __global__ __launch_bounds__(256) void adapt_apply_kernel(
   }
   if (r < ccount[dict]) {
     const int j = cand[(size_t)dict * M + r];
-    const uint8_t *xr = X + gv * ROWB;
-    double x[PER];
-    double ss = 0.0;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      x[p] = (double)elem_f<DT>(xr, lane + 64 * p);
-      ss += x[p] * x[p];
-    }
-    const double nrm = __builtin_sqrt(wave_sum_d(ss));
-    uint8_t *arow = atoms + ((size_t)dict * N + j) * ROWB;
-    double a[PER];
-    double g = 0.0, ax = 0.0;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int i = lane + 64 * p;
-      const uint32_t bits = double_to_storage_bits<DT>(x[p] / nrm);
-      if constexpr (DT == DT_F32) {
-        reinterpret_cast<uint32_t *>(arow)[i] = bits;
-        a[p] = (double)__uint_as_float(bits);
-      } else {
-        reinterpret_cast<uint16_t *>(arow)[i] = (uint16_t)bits;
-        a[p] = (double)(DT == DT_F16 ? f16_bits_to_float(bits) : bf16_bits_to_float(bits));
-      }
-      g += a[p] * a[p];
-      ax += a[p] * x[p];
-    }
-    g = wave_sum_d(g);
-    ax = wave_sum_d(ax);
-    const double c = ax / ((1.0 + (double)ridge_rel) * g + (double)ridge_abs);
-    double rr = 0.0;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const double d = x[p] - c * a[p];
-      rr += d * d;
-    }
-    rr = wave_sum_d(rr);
+    float c, e;
+    recode_onto_new_atom<DT, D>(atoms + ((size_t)dict * N + j) * ROWB, X + gv * ROWB, ridge_abs,
+                                ridge_rel, lane, c, e);
     if (lane < s) {
       idx[gv * s + lane] = lane == 0 ? j : -1;
-      coef[gv * s + lane] = lane == 0 ? (float)c : 0.f;
+      coef[gv * s + lane] = lane == 0 ? c : 0.f;
     }
     if (lane == 0) {
       usage[(size_t)dict * N + j] = 1u;
-      relerr[gv] = (float)(__builtin_sqrt(rr) / nrm);
+      relerr[gv] = e;
       flags[gv] = flags[gv] | FLAG_REPLACED;
       replaced[gv] = j;
     }
@@ -220,6 +233,125 @@ __global__ __launch_bounds__(256) void adapt_apply_kernel(
       replaced[gv] = -1;
     }
   }
+}
+
+
+// The whole commit of one dictionary in one workgroup, for steps of at most FUSED_MAXM rows
+// and dictionaries of at most FUSED_MAXN atoms (decode steps): the dictionary's usage counters
+// and touched marks live in LDS, and mark, rank, candidate listing and apply run as phases of
+// one kernel with the same rules (and results) as the separate kernels above.
+constexpr int FUSED_MAXN = 16384;
+constexpr int FUSED_MAXM = 4096;
+
+template <int DT, int D>
+__global__ __launch_bounds__(SEL_THREADS) void adapt_fused_kernel(
+    uint8_t *__restrict__ atoms, uint32_t *__restrict__ usage, const uint8_t *__restrict__ X,
+    int N, int M, int s, float ridge_abs, float ridge_rel, uint32_t tau_c,
+    int32_t *__restrict__ idx, float *__restrict__ coef, float *__restrict__ relerr,
+    uint8_t *__restrict__ flags, int32_t *__restrict__ replaced, int32_t *__restrict__ n_atoms) {
+  constexpr int ROWB = D * Elem<DT>::bytes;
+  __shared__ uint32_t s_u[FUSED_MAXN];
+  __shared__ uint8_t s_t[FUSED_MAXN];
+  __shared__ int s_trig[FUSED_MAXM];
+  __shared__ int s_cand[FUSED_MAXM];
+  __shared__ int s_w[SEL_WAVES];
+  __shared__ uint32_t s_m[SEL_WAVES];
+  const int dict = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row0 = (size_t)dict * M;
+  uint32_t *ug = usage + (size_t)dict * N;
+
+  for (int j = tid; j < N; j += SEL_THREADS) {
+    s_u[j] = ug[j];
+    s_t[j] = 0;
+  }
+  __syncthreads();
+  // mark: every atom of every code is touched; non-triggering codes commit their usage
+  for (int e = tid; e < M * s; e += SEL_THREADS) {
+    const int m = e / s;
+    const uint8_t fl = flags[row0 + m];
+    if (fl & FLAG_NONFINITE) continue;
+    const int j = idx[row0 * s + e];
+    if (j < 0 || j >= N) continue;
+    s_t[j] = 1;
+    if (!(fl & FLAG_TRIGGER)) atomicAdd(&s_u[j], 1u);
+  }
+  // triggering rows in row order
+  int T = 0;
+  for (int m0 = 0; m0 < M; m0 += SEL_THREADS) {
+    const int m = m0 + tid;
+    const bool t = m < M && (flags[row0 + m] & FLAG_TRIGGER);
+    int prefix;
+    const int total = block_prefix(t, s_w, prefix);   // its barrier also closes the mark phase
+    if (t) s_trig[T + prefix] = m;
+    T += total;
+  }
+  // candidates: the next free slots (append-only growth) or the inactive atoms in (usage, index)
+  // order, one usage level at a time
+  int count = 0;
+  if (n_atoms) {
+    int n0 = n_atoms[dict];
+    n0 = n0 < 0 ? 0 : (n0 > N ? N : n0);
+    count = T < N - n0 ? T : N - n0;
+    for (int k = tid; k < count; k += SEL_THREADS) s_cand[k] = n0 + k;
+    __syncthreads();   // every thread has read n_atoms[dict]
+    if (tid == 0) n_atoms[dict] = n0 + count;
+  } else {
+    unsigned long long floor_u = 0;
+    while (count < T && floor_u < tau_c) {
+      uint32_t mine = 0xffffffffu;
+      for (int j = tid; j < N; j += SEL_THREADS) {
+        const uint32_t uj = s_u[j];
+        if (uj < tau_c && uj >= floor_u && !s_t[j]) mine = uj < mine ? uj : mine;
+      }
+      const uint32_t level = block_min_u32(mine, s_m);
+      if (level == 0xffffffffu) break;
+      for (int j0 = 0; j0 < N && count < T; j0 += SEL_THREADS) {
+        const int j = j0 + tid;
+        const bool c = j < N && s_u[j] == level && !s_t[j];
+        int prefix;
+        const int total = block_prefix(c, s_w, prefix);
+        if (c && count + prefix < T) s_cand[count + prefix] = j;
+        count += total;
+      }
+      floor_u = (unsigned long long)level + 1ull;
+    }
+    count = count < T ? count : T;
+  }
+  __syncthreads();
+  for (int m = tid; m < M; m += SEL_THREADS)
+    if (!(flags[row0 + m] & FLAG_TRIGGER)) replaced[row0 + m] = -1;
+  // apply: one wave per triggering row
+  for (int k = wave; k < T; k += SEL_WAVES) {
+    const size_t gv = row0 + s_trig[k];
+    if (k < count) {
+      const int j = s_cand[k];
+      float c, e;
+      recode_onto_new_atom<DT, D>(atoms + ((size_t)dict * N + j) * ROWB, X + gv * ROWB,
+                                  ridge_abs, ridge_rel, lane, c, e);
+      if (lane < s) {
+        idx[gv * s + lane] = lane == 0 ? j : -1;
+        coef[gv * s + lane] = lane == 0 ? c : 0.f;
+      }
+      if (lane == 0) {
+        s_u[j] = 1u;
+        relerr[gv] = e;
+        flags[gv] = flags[gv] | FLAG_REPLACED;
+        replaced[gv] = j;
+      }
+    } else {
+      if (lane < s) {
+        const int jj = idx[gv * s + lane];
+        if (jj >= 0 && jj < N) atomicAdd(&s_u[jj], 1u);
+      }
+      if (lane == 0) {
+        flags[gv] = flags[gv] | FLAG_EXHAUSTED;
+        replaced[gv] = -1;
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < N; j += SEL_THREADS) ug[j] = s_u[j];
 }
 
 template <int DT, int D, int ODT>
@@ -251,6 +383,19 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
                         int32_t *replaced, uint8_t *touched, int touched_stride, int32_t *rank,
                         int32_t *cand, int32_t *ccount, int32_t *n_atoms, hipStream_t stream) {
   const size_t G = (size_t)num_dicts * M;
+  uint8_t *A = static_cast<uint8_t *>(atoms);
+  const uint8_t *Xb = static_cast<const uint8_t *>(X);
+  if (M <= FUSED_MAXM && N <= FUSED_MAXN) {
+#define LF(DT, D)                                                                                  \
+  hipLaunchKernelGGL((adapt_fused_kernel<DT, D>), dim3(num_dicts), dim3(SEL_THREADS), 0, stream, A, \
+                     usage, Xb, N, M, s, ridge_abs, ridge_rel, tau_c, idx, coef, relerr, flags,   \
+                     replaced, n_atoms)
+    if (dtype == DT_F32) { if (d == 64) LF(DT_F32, 64); else LF(DT_F32, 128); }
+    else if (dtype == DT_F16) { if (d == 64) LF(DT_F16, 64); else LF(DT_F16, 128); }
+    else { if (d == 64) LF(DT_BF16, 64); else LF(DT_BF16, 128); }
+#undef LF
+    return hipGetLastError();
+  }
   const size_t words = (size_t)num_dicts * touched_stride / 4;
   hipLaunchKernelGGL(adapt_clear_kernel, dim3((unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096)),
                      dim3(256), 0, stream, reinterpret_cast<uint32_t *>(touched), words);
@@ -258,8 +403,6 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
                      flags, usage, touched, touched_stride, N, M, s, G);
   hipLaunchKernelGGL(adapt_select_kernel, dim3(num_dicts), dim3(SEL_THREADS), 0, stream, usage,
                      touched, touched_stride, flags, N, M, tau_c, rank, cand, ccount, n_atoms);
-  uint8_t *A = static_cast<uint8_t *>(atoms);
-  const uint8_t *Xb = static_cast<const uint8_t *>(X);
   dim3 grid((unsigned)((G + 3) / 4)), block(256);
 #define L(DT, D)                                                                                   \
   hipLaunchKernelGGL((adapt_apply_kernel<DT, D>), grid, block, 0, stream, A, usage, Xb, N, M, s,  \

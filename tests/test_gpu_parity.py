@@ -236,6 +236,27 @@ def test_adapt_parity_usage_levels_and_exhaustion():
     assert np.all(rep == -1)
 
 
+def test_adapt_parity_both_commit_paths():
+    """Steps of at most 4096 rows on dictionaries of at most 16384 atoms commit in one
+    workgroup per dictionary, larger ones through separate mark / select / apply kernels: both
+    paths against the oracle (N = 20000 takes the second), fixed-size and append-only."""
+    _banner("adapt, both commit paths")
+    for N in (1000, 20000):
+        w = Workload("adapt", 2, 1, 64, N, 32, 4, "f16", 1, 96, 4, 0.0, 0.25, None, 31)
+        g = SyntheticKV(w)
+        A = g.atoms()
+        X = g.batch(A, support_limit=N - 300)
+        p = fadkv.Params(n=32, s=4)
+        U = np.zeros((2, N), np.int64)
+        oc = oracle.encode(to_f64(A), to_f64(X), parity.oracle_params(p))
+        rep, _ = _compare_adapt(A, X, U, oc, p, "f16")
+        assert np.sum(rep >= 0) > 0
+        Ap = _padded(A, [N - 250, N - 200])
+        oc = oracle.encode(to_f64(Ap), to_f64(X), parity.oracle_params(p))
+        rep, _ = _compare_append(Ap, X, U, oc, p, "f16", [N - 250, N - 200])
+        assert np.sum(rep >= 0) > 0
+
+
 def test_encode_adapt_multistep_parity():
     """Eight steps of 64 vectors (supports from atoms [0,192), 20% Gaussian rows): the GPU
     state (atoms, usage) and the oracle's evolve independently and agree step by step."""
