@@ -150,12 +150,13 @@ __global__ __launch_bounds__(PL_WAVES * 64) void select_pl_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
-  // Cholesky, one row per step (lane i: Lrow = L[i][0..i-1], Lcol[m] = L[m][i], dg = L[i][i])
-  float Lrow[SMAX], Lcol[SMAX];
+  // Cholesky, one row per step (lane i: Lrow = L[i][0..i-1], dg = L[i][i]); row k of L then
+  // overwrites row k of G in LDS (that row is not read again) for the back substitution
+  float Lrow[SMAX];
 #pragma unroll
-  for (int m = 0; m < SMAX; ++m) Lrow[m] = Lcol[m] = 0.f;
+  for (int m = 0; m < SMAX; ++m) Lrow[m] = 0.f;
   float dg = 1.f;
-#pragma unroll
+#pragma unroll 8
   for (int k = 0; k < SMAX; ++k) {
     if (k < s) {
       float g = lane < k ? Gw[k * SMAX + lane] : 0.f;
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(PL_WAVES * 64) void select_pl_kernel(
         }
       }
       const float lkk = sqrtf(fmaxf(fmaf(gkk, 1.f + ridge_rel, ridge_abs) - sumsq, 1e-30f));
-      if (lane < k) Lcol[k] = mine;
+      if (lane < k) Gw[k * SMAX + lane] = mine;
       if (lane == k) dg = lkk;
     }
   }
@@ -186,13 +187,16 @@ __global__ __launch_bounds__(PL_WAVES * 64) void select_pl_kernel(
       if (lane > m) b = fmaf(-Lrow[m], ym, b);
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   float c = 0.f;
 #pragma unroll
   for (int m = SMAX - 1; m >= 0; --m) {
     if (m < s) {
       const float cm = __shfl(y, m) / __shfl(dg, m);
       if (lane == m) c = cm;
-      if (lane < m) y = fmaf(-Lcol[m], cm, y);
+      if (lane < m) y = fmaf(-Gw[m * SMAX + lane], cm, y);
     }
   }
 
