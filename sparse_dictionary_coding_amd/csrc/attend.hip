@@ -7,7 +7,8 @@
 //                   x 128 atoms per workgroup
 //   attend_softmax  one workgroup per (row, query group): qd rows in LDS, a max pass and an
 //                   exp/sum/scatter pass over the row's tokens (s LDS gathers per token and
-//                   query, fp32 LDS atomics onto w), then w / sum written over qd
+//                   query, exact 64-bit fixed-point LDS atomics onto w), then w / sum written
+//                   over qd
 //   attend_out      part[range][query] = w[query][range] . D_V[range] for 32 queries x 128 atoms
 //                   per workgroup (fp32 register tiles over LDS-staged chunks)
 //   attend_reduce   out = sum over the ranges of part
@@ -46,7 +47,8 @@ constexpr int QD_ATOMS = 128;      // 8 tiles of 16 atoms, two per wave
 constexpr int SM_THREADS = 1024;   // 16 waves: four per SIMD hide the code loads
 constexpr int SM_GMAX = 8;         // queries per softmax workgroup
 constexpr int SM_CH = 8;           // slots loaded together
-constexpr int SM_LDS_FLOATS = 32768;   // qd rows + weights: 128 KB
+constexpr int SM_LDS_FLOATS = 32768;   // qd rows + fp32 weights: 128 KB
+constexpr int SM_LDS_FIXED = 156 * 1024;   // qd rows + 64-bit fixed-point weights
 constexpr int OUT_QUERIES = 32;
 constexpr int OUT_ATOMS = 128;
 
@@ -156,14 +158,25 @@ __device__ __forceinline__ void logits(const int32_t *__restrict__ idx,
 }
 
 // One workgroup per (row, group of up to SM_GMAX queries).
+//
+// FIXED: the value weights are accumulated as 64-bit integers, each contribution p_t cV[t][k]
+// (fp32) scaled by 2^sh and converted exactly; sh is the largest power of two that keeps
+// len * max|cV| * 2^sh below 2^61, so the integer sums cannot overflow and are exact (LDS
+// integer atomics run several times faster than fp32 ones).  Otherwise fp32 LDS atomics (the
+// fallback when the 8-byte accumulators of N atoms do not fit the LDS budget).
+template <bool FIXED>
 __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
     const int32_t *__restrict__ k_idx, const float *__restrict__ k_coef,
     const int32_t *__restrict__ v_idx, const float *__restrict__ v_coef,
     const int32_t *__restrict__ lens, int T, int s, int N, int G, int gw, float scale,
     float *__restrict__ ws) {
-  extern __shared__ float s_lds[];
+  // dynamic LDS starts after the static variables: the 16-byte alignment keeps the 64-bit
+  // weights below 8-byte aligned whatever the static part adds up to
+  extern __shared__ __attribute__((aligned(16))) float s_lds[];
   __shared__ float s_red[SM_THREADS / 64][SM_GMAX];
+  __shared__ float s_cred[SM_THREADS / 64];
   __shared__ float s_m[SM_GMAX], s_sum[SM_GMAX];
+  __shared__ int s_sh;
   const int r = blockIdx.x;
   const int g0 = blockIdx.y * gw;
   const int gn = min(gw, G - g0);
@@ -171,17 +184,22 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
   int L = lens[r];
   L = L < 0 ? 0 : (L > T ? T : L);
   float *qs = s_lds;                 // [gn][N] qd rows
-  float *wv = s_lds + (size_t)gw * N;   // [gn][N] value-atom weights
+  float *wv = s_lds + (size_t)gw * N;   // [gn][N] value-atom weights (fp32)
+  // FIXED: [gn][N] 64-bit weights after the qd rows, 8-byte aligned
+  unsigned long long *wq =
+      reinterpret_cast<unsigned long long *>(s_lds + (((size_t)gw * N + 1) & ~(size_t)1));
   float *rows = ws + ((size_t)r * G + g0) * N;
   for (int i = tid; i < gn * N; i += SM_THREADS) {
     qs[i] = rows[i];
-    wv[i] = 0.f;
+    if constexpr (FIXED) wq[i] = 0ull;
+    else wv[i] = 0.f;
   }
   __syncthreads();
   const size_t cbase = (size_t)r * T * s;
 
-  // pass 1: the largest logit of every query
+  // pass 1: the largest logit of every query (and, FIXED, the largest |cV|)
   float mx[SM_GMAX];
+  float cmax = 0.f;
 #pragma unroll
   for (int g = 0; g < SM_GMAX; ++g) mx[g] = -__builtin_inff();
   for (int t = tid; t < L; t += SM_THREADS) {
@@ -189,6 +207,12 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
     logits(k_idx + cbase + (size_t)t * s, k_coef + cbase + (size_t)t * s, s, N, gn, qs, z);
 #pragma unroll
     for (int g = 0; g < SM_GMAX; ++g) mx[g] = fmaxf(mx[g], z[g] * scale);
+    if constexpr (FIXED) {
+      for (int k = 0; k < s; ++k) {
+        const int j = v_idx[cbase + (size_t)t * s + k];
+        if (j >= 0 && j < N) cmax = fmaxf(cmax, fabsf(v_coef[cbase + (size_t)t * s + k]));
+      }
+    }
   }
 #pragma unroll
   for (int g = 0; g < SM_GMAX; ++g) {
@@ -197,13 +221,30 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     if (lane == 0) s_red[wave][g] = v;
   }
+  if constexpr (FIXED) {
+    float v = cmax;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if (lane == 0) s_cred[wave] = v;
+  }
   __syncthreads();
   if (tid < SM_GMAX) {
     float v = s_red[0][tid];
     for (int w = 1; w < SM_THREADS / 64; ++w) v = fmaxf(v, s_red[w][tid]);
     s_m[tid] = v;
   }
+  if (FIXED && tid == 0) {
+    float v = 0.f;
+    for (int w = 0; w < SM_THREADS / 64; ++w) v = fmaxf(v, s_cred[w]);
+    // len * cmax * 2^sh < 2^61: with len * cmax in [2^(e-1), 2^e), sh = 61 - e
+    const float bound = (float)L * v;
+    int e = 0;
+    if (bound > 0.f && __builtin_isfinite(bound)) (void)__builtin_frexpf(bound, &e);
+    int sh = 61 - e;
+    s_sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
+  }
   __syncthreads();
+  const int sh = FIXED ? s_sh : 0;
 
   // pass 2: p_t = exp(z_t - max), the sums, and the scatter of p_t cV onto the value atoms
   float m[SM_GMAX], sum[SM_GMAX];
@@ -230,8 +271,16 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
       for (int k = 0; k < SM_CH; ++k) {
         if (vj[k] >= 0 && vj[k] < N) {
 #pragma unroll
-          for (int g = 0; g < SM_GMAX; ++g)
-            if (g < gn) atomicAdd(&wv[g * N + vj[k]], p[g] * vcf[k]);
+          for (int g = 0; g < SM_GMAX; ++g) {
+            if (g < gn) {
+              if constexpr (FIXED) {
+                const long long qv = __double2ll_rn((double)__builtin_ldexpf(p[g] * vcf[k], sh));
+                atomicAdd(&wq[g * N + vj[k]], (unsigned long long)qv);
+              } else {
+                atomicAdd(&wv[g * N + vj[k]], p[g] * vcf[k]);
+              }
+            }
+          }
         }
       }
     }
@@ -251,7 +300,10 @@ __global__ __launch_bounds__(SM_THREADS) void attend_softmax_kernel(
   // weights / sum over the qd rows (this workgroup owns them); a row without tokens gets 0
   for (int i = tid; i < gn * N; i += SM_THREADS) {
     const float S = s_sum[i / N];
-    rows[i] = S > 0.f ? wv[i] / S : 0.f;
+    float wi;
+    if constexpr (FIXED) wi = (float)__builtin_ldexp((double)(long long)wq[i], -sh);
+    else wi = wv[i];
+    rows[i] = S > 0.f ? wi / S : 0.f;
   }
 }
 
@@ -350,16 +402,23 @@ hipError_t launch_attend(int dtype, int d, const void *dictK, const void *dictV,
   const uint8_t *V = static_cast<const uint8_t *>(dictV);
   const uint8_t *Q = static_cast<const uint8_t *>(q);
   dim3 g1((unsigned)((RG + QD_QUERIES - 1) / QD_QUERIES), (unsigned)((N + QD_ATOMS - 1) / QD_ATOMS));
-  // queries per softmax workgroup: qd rows and weights of gw queries fit the LDS budget
-  int gw = SM_LDS_FLOATS / (2 * N);
+  // queries per softmax workgroup: qd rows and weights of gw queries fit the LDS budget (8-byte
+  // fixed-point weights when at least one query fits that way, else fp32 weights)
+  const bool fixed = (size_t)N * 12 + 4 <= (size_t)SM_LDS_FIXED;
+  int gw = fixed ? (int)((size_t)(SM_LDS_FIXED - 4) / ((size_t)N * 12)) : SM_LDS_FLOATS / (2 * N);
   gw = gw < 1 ? 1 : (gw > SM_GMAX ? SM_GMAX : gw);
   gw = gw > G ? G : gw;
   dim3 g2((unsigned)R, (unsigned)((G + gw - 1) / gw));
-  const size_t lds2 = (size_t)2 * gw * N * sizeof(float);   // <= 128 KB for N <= 16384
+  // qd rows (padded to 8 bytes) + weights: <= 156 KB fixed-point / 128 KB fp32
+  const size_t lds2 = fixed ? (((size_t)gw * N + 1) & ~(size_t)1) * 4 + (size_t)gw * N * 8
+                            : (size_t)gw * N * 8;
   if (lds2 > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attend_softmax_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(SM_LDS_FLOATS * sizeof(float)));
+    const hipError_t e = fixed
+        ? hipFuncSetAttribute(reinterpret_cast<const void *>(attend_softmax_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SM_LDS_FIXED)
+        : hipFuncSetAttribute(reinterpret_cast<const void *>(attend_softmax_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(SM_LDS_FLOATS * sizeof(float)));
     if (e != hipSuccess) return e;
   }
   const int nranges = (N + OUT_ATOMS - 1) / OUT_ATOMS;
@@ -370,8 +429,12 @@ hipError_t launch_attend(int dtype, int d, const void *dictK, const void *dictV,
 #define L(DT, D)                                                                                \
   do {                                                                                          \
     hipLaunchKernelGGL((attend_qd_kernel<DT, D>), g1, dim3(256), 0, stream, K, Q, RG, N, ws);    \
-    hipLaunchKernelGGL(attend_softmax_kernel, g2, dim3(SM_THREADS), lds2, stream, k_idx, k_coef, \
-                       v_idx, v_coef, lens, T, s, N, G, gw, scale, ws);                         \
+    if (fixed)                                                                                  \
+      hipLaunchKernelGGL(attend_softmax_kernel<true>, g2, dim3(SM_THREADS), lds2, stream, k_idx, \
+                         k_coef, v_idx, v_coef, lens, T, s, N, G, gw, scale, ws);               \
+    else                                                                                        \
+      hipLaunchKernelGGL(attend_softmax_kernel<false>, g2, dim3(SM_THREADS), lds2, stream, k_idx,\
+                         k_coef, v_idx, v_coef, lens, T, s, N, G, gw, scale, ws);               \
     hipLaunchKernelGGL((attend_out_kernel<DT, D>), g3, dim3(256), 0, stream, V, ws, RG, N, part); \
     hipLaunchKernelGGL(attend_reduce_kernel, g4, dim3(256), 0, stream, part, nranges, total, out); \
   } while (0)

@@ -35,3 +35,25 @@ def test_m0_written_only_by_lds_copies(tmp_path, name):
         assert lines[i + 2].startswith("global_load_lds_dwordx4 "), lines[i + 2]
         copies += 1
     assert copies > 0
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_softmax_dynamic_lds_is_8_byte_aligned(tmp_path):
+    """The attention softmax keeps 64-bit fixed-point weights in dynamic LDS, which starts right
+    after the kernel's static LDS: that static size must keep the dynamic base 8-byte aligned
+    (misaligned 64-bit LDS accesses fault)."""
+    src = os.path.join(build.CSRC, "attend.hip")
+    out = tmp_path / "attend.s"
+    cmd = [HIPCC, *build.HIPCC_FLAGS, f"-I{build.INCLUDE}", f"-I{build.CSRC}",
+           "--cuda-device-only", "-S", src, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    sizes = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)\n((?:.*\n)*?)\s+\.end_amdhsa_kernel", text):
+        if "attend_softmax_kernel" in m.group(1):
+            g = re.search(r"amdhsa_group_segment_fixed_size (\d+)", m.group(2))
+            sizes[m.group(1)] = int(g.group(1))
+    assert sizes, "softmax kernels not found"
+    for name, size in sizes.items():
+        assert size % 8 == 0, (name, size)

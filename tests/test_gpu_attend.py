@@ -5,7 +5,8 @@ Codes are seeded and synthetic (random atoms per slot, some empty slots, N(0,1) 
 queries and dictionaries are stored in the dictionary dtype and fed to the oracle as those exact
 values.  Tolerance: the kernels compute q . D_K^T with fp32 accumulation of exact 16-bit
 products, logits as s-term fp32 sums, exp with a relative error of a few ulp, and value
-weights accumulated in fp32 (atomics, any order) over up to T*s terms, then a d-wide fp32 dot
+weights accumulated exactly as 64-bit fixed point from fp32 products (in fp32 atomics, any
+order, when N is too large for that), over up to T*s terms, then a d-wide fp32 dot
 with D_V over N atoms.  Each stage contributes O(1e-6) relative error for these sizes, so
 |out - ref| <= 2e-4 * max|ref| per (row, query) plus 1e-6 leaves a wide margin while any
 indexing, scaling or normalisation mistake shows up at O(1).
@@ -73,6 +74,7 @@ SHAPES = [
     ("f16", 64, 1000, 5, 7, 33, 1),
     ("bf16", 128, 8192, 16, 5, 120, 4),
     ("f32", 128, 777, 3, 6, 64, 5),
+    ("bf16", 64, 16384, 8, 3, 50, 2),      # largest N: fp32 weight accumulation in LDS
 ]
 
 
