@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--select", default="gm", choices=["gm", "pl"])
     ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 3B prefill measurement added to the default decode line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--path", default="encode", choices=["encode", "attend", "growth", "omp"],
                     help="encode: the encoder hot path (default); attend: decode attention of "
@@ -508,23 +510,9 @@ def bench_omp(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(dictionaries shard by layer with no communication); run with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.path == "attend":
-        bench_attend(args)
-        return
-    if args.path == "growth":
-        bench_growth(args)
-        return
-    if args.path == "omp":
-        bench_omp(args)
-        return
-
+def measure_encode(args, name, steps, warmup):
+    """Time `steps` encode + commit steps of workload `name` (after `warmup` untimed ones) and
+    return (workload, result dict) as printed by the default path."""
     import torch
 
     from sparse_dictionary_coding_amd import fadkv, synth
@@ -532,7 +520,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[name]
     p = fadkv.Params(n=w.n, s=w.s, select=args.select)
     T, M, N, d = w.num_dicts, w.M, w.N, w.d
     esize = 2 if w.dtype != "f32" else 4
@@ -544,7 +532,7 @@ def main():
     base_atoms = gen.atoms()
     sets = [base_atoms.clone() for _ in range(R)]
     usages = [torch.zeros(T, N, dtype=torch.int32, device=dev) for _ in range(R)]
-    n_batches = min(args.steps + args.warmup, 16 if M * T <= 65536 else 1)
+    n_batches = min(steps + warmup, 16 if M * T <= 65536 else 1)
     batches = [gen.batch(base_atoms, step=i) for i in range(n_batches)]
     pool = fadkv.Pool.empty(T, M, w.n, dev)
     codes = fadkv.Codes.empty(T, M, w.s, dev)
@@ -574,14 +562,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for k in range(args.warmup):
+    for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k, evs[k])
+    for k in range(steps):
+        step(warmup + k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -589,10 +577,10 @@ def main():
     for e in evs:
         for i in range(3):
             stage_ms[i] += e[i].elapsed_time(e[i + 1])
-    stage_ms = [x / args.steps for x in stage_ms]
+    stage_ms = [x / steps for x in stage_ms]
     G = T * M
     vec_per_step = G
-    value = vec_per_step * args.steps / wall
+    value = vec_per_step * steps / wall
 
     # algorithmic work per launch
     screen_flops = 2.0 * N * d * G
@@ -623,7 +611,7 @@ def main():
 
     out = {
         "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "steps": steps, "warmup": warmup, "ms_per_step": wall * 1e3 / steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "num_dicts": T, "vectors_per_dict": M, "N": N, "n": w.n,
@@ -637,6 +625,39 @@ def main():
                        "frac": screen_gbs / HBM_PEAK_GBS},
         "last_step": {"triggers": trig, "replaced": rep},
     }
+    return w, out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(dictionaries shard by layer with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.path == "attend":
+        bench_attend(args)
+        return
+    if args.path == "growth":
+        bench_growth(args)
+        return
+    if args.path == "omp":
+        bench_omp(args)
+        return
+
+    w, out = measure_encode(args, args.workload, args.steps, args.warmup)
+    if args.workload == "llama3b_decode" and not args.no_prefill:
+        # the prefill configuration of the same model, reported beside the decode step
+        import torch
+        torch.cuda.empty_cache()
+        wp, pre = measure_encode(args, "llama3b_prefill", 3, 1)
+        out["prefill"] = {k: pre[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                               "roofline", "kernels")}
+        out["prefill"]["screen_mfma"] = {
+            "achieved": pre["kernels"]["screen_topn"]["flops"] / (pre["kernels"]["screen_topn"]["ms"] * 1e-3) / 1e12,
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        out["prefill"]["screen_mfma"]["frac"] = out["prefill"]["screen_mfma"]["achieved"] / MFMA_BF16_PEAK_TFLOPS
+        out["prefill"]["steps"], out["prefill"]["warmup"] = 3, 1
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.select, args.cpu_seconds)
     print(json.dumps(out), flush=True)
