@@ -356,22 +356,38 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
 
   // ---- resolve boundaries; refine the rest (rare) -------------------------------------------
   for (int pass = 0;; ++pass) {
-    // vectors that collected this pass: take the `need` largest keys of the boundary buffer
-    for (int slot = tid; slot < VT * CAP; slot += THREADS) {
-      const int v = slot / CAP, e = slot % CAP;
-      const int st = s_state[v];
-      const int cnt = s_bcnt[v] < CAP ? s_bcnt[v] : CAP;
-      if ((st != ST_COLLECT && st != ST_RCOLLECT) || e >= cnt) continue;
+    // vectors that collected this pass: take the `need` largest keys of the boundary buffer.
+    // One wave per vector; lane e holds entries e and e + 64 in registers, and each entry's
+    // rank (the number of larger keys; keys are unique) counts the keys broadcast lane by lane.
+    for (int v = wave; v < VT; v += WAVES) {
+      const int st = __builtin_amdgcn_readfirstlane(s_state[v]);
+      if (st != ST_COLLECT && st != ST_RCOLLECT) continue;
+      const int cnt = __builtin_amdgcn_readfirstlane(s_bcnt[v] < CAP ? s_bcnt[v] : CAP);
       const uint32_t *reg = s_reg + v * REGW;
-      const u64 Ke = comp_key(reg[e] & 0x7fffffffu, (int)reg[CAP + e]);
-      int rank = 0;
-      for (int q = 0; q < cnt; ++q) rank += comp_key(reg[q] & 0x7fffffffu, (int)reg[CAP + q]) > Ke;
+      const int e0 = lane, e1 = lane + 64;
+      const u64 K0 = e0 < cnt ? comp_key(reg[e0] & 0x7fffffffu, (int)reg[CAP + e0]) : 0ull;
+      const u64 K1 = e1 < cnt ? comp_key(reg[e1] & 0x7fffffffu, (int)reg[CAP + e1]) : 0ull;
+      int r0 = 0, r1 = 0;
+      for (int q = 0; q < cnt; ++q) {
+        const u64 src = q < 64 ? K0 : K1;
+        const int ql = q & 63;
+        const uint32_t qh = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(src >> 32), ql);
+        const uint32_t ql32 = (uint32_t)__builtin_amdgcn_readlane((uint32_t)src, ql);
+        const u64 Kq = ((u64)qh << 32) | (u64)ql32;
+        r0 += Kq > K0;
+        r1 += Kq > K1;
+      }
       const int need = s_need[v];
-      if (rank < need && need <= n) {
+      if (need <= n) {
         const size_t row = (vbase + v) * (size_t)n;
-        const int pos = n - need + rank;
-        pool_idx[row + pos] = (uint16_t)reg[CAP + e];
-        pool_sig[row + pos] = __uint_as_float(reg[e]);
+        if (e0 < cnt && r0 < need) {
+          pool_idx[row + n - need + r0] = (uint16_t)reg[CAP + e0];
+          pool_sig[row + n - need + r0] = __uint_as_float(reg[e0]);
+        }
+        if (e1 < cnt && r1 < need) {
+          pool_idx[row + n - need + r1] = (uint16_t)reg[CAP + e1];
+          pool_sig[row + n - need + r1] = __uint_as_float(reg[e1]);
+        }
       }
     }
     __syncthreads();
