@@ -43,6 +43,7 @@ constexpr int DISCARD = RB;
 constexpr int TPV = THREADS / VT;    // threads per vector in the histogram scans (16)
 constexpr int SHIFT0 = 18;       // key >> 18 = 8 exponent bits + 5 mantissa bits
 constexpr int TOP0 = 237;        // level-0 bin of |score| ~ ||x|| is TOP0; 18 bins (~1.5x) above
+constexpr int QCAP = 128;        // per-wave hit queue of the collect sweep (a ring)
 
 enum { ST_IDLE = 0, ST_HIST0, ST_COLLECT, ST_REFINE, ST_RCOLLECT };
 enum { PASS_HIST0 = 0, PASS_COLLECT = 1, PASS_GENERIC = 2 };
@@ -70,7 +71,40 @@ struct Shared {
   uint32_t *reg;            // VT regions of REGW words
   int *above;
   int *bcnt;
+  const uint32_t *hi32;     // per vector: lowest key above its boundary bin
+  uint16_t *pidx0;          // pool rows of the workgroup's first vector
+  float *psig0;
 };
+
+// A wave's collect-sweep hits wait in its LDS ring (score bits, atom | vector << 16) until 64
+// are there; then every lane takes one, reserves its slot (pool or boundary buffer) with one
+// LDS atomic and stores it.  head and len are wave-uniform.
+struct HitQueue {
+  uint2 *ring;
+  int head, len;
+};
+
+__device__ __forceinline__ void flush_hits(int count, HitQueue &hq, int lane, int n,
+                                           const Shared &sh) {
+  if (lane < count) {
+    const uint2 e = hq.ring[(hq.head + lane) & (QCAP - 1)];
+    const int atom = (int)(e.y & 0xFFFFu), vi = (int)(e.y >> 16);
+    const bool hi = (e.x & 0x7fffffffu) >= sh.hi32[vi];
+    const int pos = atomicAdd(hi ? &sh.above[vi] : &sh.bcnt[vi], 1);
+    if (hi) {
+      if (pos < n) {
+        sh.pidx0[(size_t)vi * n + pos] = (uint16_t)atom;
+        sh.psig0[(size_t)vi * n + pos] = __uint_as_float(e.x);
+      }
+    } else if (pos < CAP) {
+      uint32_t *reg = sh.reg + vi * REGW;
+      reg[pos] = e.x;
+      reg[CAP + pos] = (uint32_t)atom;
+    }
+  }
+  hq.head = (hq.head + count) & (QCAP - 1);
+  hq.len -= count;
+}
 
 template <int PASS, bool CHECK>
 __device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, int n,
@@ -110,11 +144,12 @@ __device__ __forceinline__ void process(const float4_t &acc, int atom0, int N, i
 
 // Collect pass over one tile for both vectors.  Hits (|score| at or above the boundary bin)
 // are rare, so each lane first gathers its eight hit flags into a mask and the wave then loops
-// over the hits, one per lane and round (rounds = the largest hit count of a lane, not eight).
+// over the hits, one per lane and round (rounds = the largest hit count of a lane, not eight),
+// appending them to the wave's hit queue.
 template <bool CHECK>
 __device__ __forceinline__ void collect_tile(const float4_t &acc0, const float4_t &acc1, int atom0,
                                              int N, int n, const VecState (&vs)[2],
-                                             const Shared &sh) {
+                                             const Shared &sh, HitQueue &hq, int lane) {
   const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
   uint32_t m = 0;
 #pragma unroll
@@ -124,7 +159,9 @@ __device__ __forceinline__ void collect_tile(const float4_t &acc0, const float4_
     const bool ok = q.active && (!CHECK || atom0 + (b & 3) < N);
     m |= (ok && key >= q.lo32) ? 1u << b : 0u;
   }
-  while (__builtin_amdgcn_ballot_w64(m != 0)) {
+  for (;;) {
+    const u64 hm = __builtin_amdgcn_ballot_w64(m != 0);
+    if (!hm) break;
     if (m) {
       const int b = __builtin_ctz(m);
       m &= m - 1;
@@ -134,23 +171,14 @@ __device__ __forceinline__ void collect_tile(const float4_t &acc0, const float4_
       const float c1 = b1 ? (b0 ? v[7] : v[6]) : (b0 ? v[5] : v[4]);
       const float sc = b2 ? c1 : c0;
       const int vi = b2 ? vs[1].vi : vs[0].vi;
-      const uint32_t hi32 = b2 ? vs[1].hi32 : vs[0].hi32;
       const int atom = atom0 + (b & 3);
-      const bool hi = (__float_as_uint(sc) & 0x7fffffffu) >= hi32;
-      const int pos = atomicAdd(hi ? &sh.above[vi] : &sh.bcnt[vi], 1);
-      if (hi) {
-        if (pos < n) {
-          uint16_t *pidx = b2 ? vs[1].pidx : vs[0].pidx;
-          float *psig = b2 ? vs[1].psig : vs[0].psig;
-          pidx[pos] = (uint16_t)atom;
-          psig[pos] = sc;
-        }
-      } else if (pos < CAP) {
-        uint32_t *reg = sh.reg + vi * REGW;
-        reg[pos] = __float_as_uint(sc);
-        reg[CAP + pos] = (uint32_t)atom;
-      }
+      const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hm >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)hm, 0u));
+      hq.ring[(hq.head + hq.len + r) & (QCAP - 1)] =
+          make_uint2(__float_as_uint(sc), (uint32_t)atom | ((uint32_t)vi << 16));
     }
+    hq.len += __popcll(hm);          // <= 63 before the round, so <= 127 < QCAP after it
+    if (hq.len >= 64) flush_hits(64, hq, lane, n, sh);
   }
 }
 
@@ -160,7 +188,8 @@ __device__ __forceinline__ void collect_tile(const float4_t &acc0, const float4_
 template <int DT, int D, int PASS, bool REV = false>
 __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, int wave, int lane,
                                       const uint4 (&b)[2][Geo<DT, D>::CH], const VecState (&vs)[2],
-                                      const Shared &sh, const uint4 *stage, uint32_t stage_lds) {
+                                      const Shared &sh, const uint4 *stage, uint32_t stage_lds,
+                                      uint2 *ring) {
   using G = Geo<DT, D>;
   const int ntiles = (N + 15) / 16;
   const int r = lane % 16, g = lane / 16;
@@ -169,6 +198,7 @@ __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, i
   if (wave >= ntiles) return;
   const int tlast = wave + (ntiles - 1 - wave) / WAVES * WAVES;
   const int tfirst = REV ? tlast : wave, step = REV ? -WAVES : WAVES;
+  HitQueue hq{ring, 0, 0};
   issue_tile<DT, D>(dict_atoms, N, tfirst, lane, off, stage_lds);
   for (int t = tfirst; REV ? t >= 0 : t < ntiles; t += step) {
     wait_vmem();   // the tile is in the stage
@@ -183,8 +213,8 @@ __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, i
     const int atom0 = t * 16 + 4 * g;
     const bool full = t * 16 + 16 <= N;
     if constexpr (PASS == PASS_COLLECT) {
-      if (full) collect_tile<false>(acc0, acc1, atom0, N, n, vs, sh);
-      else collect_tile<true>(acc0, acc1, atom0, N, n, vs, sh);
+      if (full) collect_tile<false>(acc0, acc1, atom0, N, n, vs, sh, hq, lane);
+      else collect_tile<true>(acc0, acc1, atom0, N, n, vs, sh, hq, lane);
     } else if (full) {
       if (vs[0].active) process<PASS, false>(acc0, atom0, N, n, vs[0], sh);
       if (vs[1].active) process<PASS, false>(acc1, atom0, N, n, vs[1], sh);
@@ -192,6 +222,9 @@ __device__ __forceinline__ void sweep(const uint8_t *dict_atoms, int N, int n, i
       if (vs[0].active) process<PASS, true>(acc0, atom0, N, n, vs[0], sh);
       if (vs[1].active) process<PASS, true>(acc1, atom0, N, n, vs[1], sh);
     }
+  }
+  if constexpr (PASS == PASS_COLLECT) {
+    while (hq.len > 0) flush_hits(hq.len < 64 ? hq.len : 64, hq, lane, n, sh);
   }
 }
 
@@ -209,6 +242,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
   __shared__ uint32_t s_lo32[VT], s_hi32[VT];
   __shared__ int s_state[VT], s_need[VT], s_base[VT], s_shift[VT], s_above[VT], s_bcnt[VT];
   __shared__ int s_busy;
+  __shared__ uint2 s_queue[WAVES * QCAP];
 
   // workgroup i runs on XCD i % 8; its r-th workgroup takes dictionary x + 8 * (r / B)
   const int nvb = (M + VT - 1) / VT;
@@ -220,7 +254,9 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint8_t *dict_atoms = atoms + (size_t)dict * N * G::ROWB;
   const size_t vbase = (size_t)dict * M + v0;
-  const Shared sh{s_reg, s_above, s_bcnt};
+  const Shared sh{s_reg, s_above, s_bcnt, s_hi32, pool_idx + vbase * (size_t)n,
+                  pool_sig + vbase * (size_t)n};
+  uint2 *ring = s_queue + wave * QCAP;
   uint4 *stage = s_stage + wave * G::STAGE;
   // LDS byte address of the stage (wave-uniform, for M0)
   const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(
@@ -290,7 +326,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
     vs[k].base = s_base[vs[k].vi];
     vs[k].off = vs[k].vi * REGW - vs[k].base;
   }
-  sweep<DT, D, PASS_HIST0>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
+  sweep<DT, D, PASS_HIST0>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds, ring);
   __syncthreads();
   {
     // TPV threads per vector: thread `sub` covers bins [16 sub, 16 sub + 16); a suffix sum of
@@ -351,7 +387,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
     vs[k].lo32 = s_lo32[vs[k].vi];
     vs[k].hi32 = s_hi32[vs[k].vi];
   }
-  sweep<DT, D, PASS_COLLECT, true>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
+  sweep<DT, D, PASS_COLLECT, true>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds, ring);
   __syncthreads();
 
   // ---- resolve boundaries; refine the rest (rare) -------------------------------------------
@@ -459,7 +495,7 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
       vs[k].hi = s_hi[v];
       vs[k].shift = s_shift[v];
     }
-    sweep<DT, D, PASS_GENERIC>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds);
+    sweep<DT, D, PASS_GENERIC>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds, ring);
     __syncthreads();
   }
 }
