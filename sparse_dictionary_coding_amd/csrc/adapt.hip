@@ -45,6 +45,44 @@ __global__ __launch_bounds__(256) void adapt_mark_kernel(const int32_t *__restri
   }
 }
 
+// The same marks and usage commits for large steps, privatised per workgroup: workgroup b takes
+// rows [m0, m1) of dictionary b / chunks, counts its committed slots per atom and its touched
+// atoms in LDS (one thread per code slot), then adds every nonzero count to the global
+// counter with one atomic.  Integer sums commute, so the counters equal the per-slot
+// kernel's.  LDS: N words of counts and N bytes of marks.
+constexpr int MARK_THREADS = 256;
+constexpr int kMarkLdsMaxN = 12288;   // 48 KB of counts + 12 KB of marks
+__global__ __launch_bounds__(MARK_THREADS) void adapt_mark_lds_kernel(
+    const int32_t *__restrict__ idx, const uint8_t *__restrict__ flags,
+    uint32_t *__restrict__ usage, uint8_t *__restrict__ touched, int touched_stride, int N, int M,
+    int s, int chunks) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_cnt[];
+  uint8_t *s_tch = reinterpret_cast<uint8_t *>(s_cnt + N);
+  const int dict = blockIdx.x / chunks, c = blockIdx.x % chunks;
+  const int per = (M + chunks - 1) / chunks;
+  const int m0 = c * per, m1 = min(M, m0 + per);
+  const int words = N + (N + 3) / 4;
+  for (int i = threadIdx.x; i < words; i += MARK_THREADS) s_cnt[i] = 0u;
+  __syncthreads();
+  const size_t row0 = (size_t)dict * M;
+  const long e1 = (long)m1 * s;
+  for (long e = (long)m0 * s + threadIdx.x; e < e1; e += MARK_THREADS) {
+    const int m = (int)(e / s);
+    const uint8_t fl = flags[row0 + m];
+    if (fl & FLAG_NONFINITE) continue;
+    const int j = idx[row0 * s + e];
+    if (j < 0 || j >= N) continue;
+    s_tch[j] = 1;
+    if (!(fl & FLAG_TRIGGER)) atomicAdd(&s_cnt[j], 1u);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < N; j += MARK_THREADS) {
+    const uint32_t v = s_cnt[j];
+    if (v) atomicAdd(&usage[(size_t)dict * N + j], v);
+    if (s_tch[j]) touched[(size_t)dict * touched_stride + j] = 1;
+  }
+}
+
 namespace {
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
@@ -399,8 +437,20 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
   const size_t words = (size_t)num_dicts * touched_stride / 4;
   hipLaunchKernelGGL(adapt_clear_kernel, dim3((unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096)),
                      dim3(256), 0, stream, reinterpret_cast<uint32_t *>(touched), words);
-  hipLaunchKernelGGL(adapt_mark_kernel, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, stream, idx,
-                     flags, usage, touched, touched_stride, N, M, s, G);
+  if (N <= kMarkLdsMaxN) {
+    // about 512 workgroups over the step, at least 1024 rows each
+    int chunks = (512 + num_dicts - 1) / num_dicts;
+    const int by_rows = (M + 1023) / 1024;
+    chunks = chunks < by_rows ? chunks : by_rows;
+    chunks = chunks < 1 ? 1 : chunks;
+    const size_t lds = ((size_t)N + (N + 3) / 4) * sizeof(uint32_t);
+    hipLaunchKernelGGL(adapt_mark_lds_kernel, dim3((unsigned)(num_dicts * chunks)),
+                       dim3(MARK_THREADS), lds, stream, idx, flags, usage, touched, touched_stride,
+                       N, M, s, chunks);
+  } else {
+    hipLaunchKernelGGL(adapt_mark_kernel, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, stream,
+                       idx, flags, usage, touched, touched_stride, N, M, s, G);
+  }
   hipLaunchKernelGGL(adapt_select_kernel, dim3(num_dicts), dim3(SEL_THREADS), 0, stream, usage,
                      touched, touched_stride, flags, N, M, tau_c, rank, cand, ccount, n_atoms);
   dim3 grid((unsigned)((G + 3) / 4)), block(256);

@@ -238,22 +238,24 @@ def test_adapt_parity_usage_levels_and_exhaustion():
 
 def test_adapt_parity_both_commit_paths():
     """Steps of at most 4096 rows on dictionaries of at most 16384 atoms commit in one
-    workgroup per dictionary, larger ones through separate mark / select / apply kernels: both
-    paths against the oracle (N = 20000 takes the second), fixed-size and append-only."""
-    _banner("adapt, both commit paths")
-    for N in (1000, 20000):
-        w = Workload("adapt", 2, 1, 64, N, 32, 4, "f16", 1, 96, 4, 0.0, 0.25, None, 31)
+    workgroup per dictionary, larger ones through separate mark / select / apply kernels (the
+    mark counting in LDS per workgroup up to 12288 atoms, with one atomic per slot above): every
+    path against the oracle (N = 20000 and 96 rows: per-slot mark; N = 1000 and 4500 rows: LDS
+    mark), fixed-size and append-only."""
+    _banner("adapt, every commit path")
+    for N, M, T in ((1000, 96, 2), (20000, 96, 2), (1000, 4500, 1)):
+        w = Workload("adapt", T, 1, 64, N, 32, 4, "f16", 1, M, 4, 0.0, 0.25, None, 31)
         g = SyntheticKV(w)
         A = g.atoms()
         X = g.batch(A, support_limit=N - 300)
         p = fadkv.Params(n=32, s=4)
-        U = np.zeros((2, N), np.int64)
+        U = np.zeros((T, N), np.int64)
         oc = oracle.encode(to_f64(A), to_f64(X), parity.oracle_params(p))
         rep, _ = _compare_adapt(A, X, U, oc, p, "f16")
         assert np.sum(rep >= 0) > 0
-        Ap = _padded(A, [N - 250, N - 200])
+        Ap = _padded(A, [N - 250, N - 200][:T])
         oc = oracle.encode(to_f64(Ap), to_f64(X), parity.oracle_params(p))
-        rep, _ = _compare_append(Ap, X, U, oc, p, "f16", [N - 250, N - 200])
+        rep, _ = _compare_append(Ap, X, U, oc, p, "f16", [N - 250, N - 200][:T])
         assert np.sum(rep >= 0) > 0
 
 
