@@ -41,15 +41,24 @@ template <int DT, int D> struct RowWords {
 template <int DT, int NW>
 __device__ __forceinline__ float row_dot_uniform(const uint32_t (&a)[NW],
                                                  const uint32_t *__restrict__ row) {
+  // the row arrives in chunks of up to 32 words, each chunk's loads issued together, so a
+  // step waits on NW / 32 scalar round trips rather than one per 16 words
+  constexpr int CHUNK = NW < 32 ? NW : 32;
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int q = 0; q < NW; q += 2) {
-    if constexpr (DT == DT_F32) {
-      s0 = fmaf(__uint_as_float(a[q]), __uint_as_float(row[q]), s0);
-      s1 = fmaf(__uint_as_float(a[q + 1]), __uint_as_float(row[q + 1]), s1);
-    } else {
-      s0 = dot2<DT>(a[q], row[q], s0);
-      s1 = dot2<DT>(a[q + 1], row[q + 1], s1);
+  for (int h = 0; h < NW; h += CHUNK) {
+    uint32_t r[CHUNK];
+#pragma unroll
+    for (int q = 0; q < CHUNK; ++q) r[q] = row[h + q];
+#pragma unroll
+    for (int q = 0; q < CHUNK; q += 2) {
+      if constexpr (DT == DT_F32) {
+        s0 = fmaf(__uint_as_float(a[h + q]), __uint_as_float(r[q]), s0);
+        s1 = fmaf(__uint_as_float(a[h + q + 1]), __uint_as_float(r[q + 1]), s1);
+      } else {
+        s0 = dot2<DT>(a[h + q], r[q], s0);
+        s1 = dot2<DT>(a[h + q + 1], r[q + 1], s1);
+      }
     }
   }
   return s0 + s1;
