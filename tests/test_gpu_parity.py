@@ -240,10 +240,10 @@ def test_adapt_parity_both_commit_paths():
     """Steps of at most 4096 rows on dictionaries of at most 16384 atoms commit in one
     workgroup per dictionary, larger ones through separate mark / select / apply kernels (the
     mark counting in LDS per workgroup up to 12288 atoms, with one atomic per slot above): every
-    path against the oracle (N = 20000 and 96 rows: per-slot mark; N = 1000 and 4500 rows: LDS
-    mark), fixed-size and append-only."""
+    path against the oracle (N = 20000 and 96 rows: per-slot mark; N = 1000 and N = 12288, the
+    largest the LDS counters take, with 4500 rows: LDS mark), fixed-size and append-only."""
     _banner("adapt, every commit path")
-    for N, M, T in ((1000, 96, 2), (20000, 96, 2), (1000, 4500, 1)):
+    for N, M, T in ((1000, 96, 2), (20000, 96, 2), (1000, 4500, 1), (12288, 4500, 1)):
         w = Workload("adapt", T, 1, 64, N, 32, 4, "f16", 1, M, 4, 0.0, 0.25, None, 31)
         g = SyntheticKV(w)
         A = g.atoms()
