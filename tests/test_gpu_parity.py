@@ -500,3 +500,13 @@ def test_full_size_llama3b_decode_pl_sampled():
 
 def test_full_size_llama8b_decode_pl_sampled():
     _full_size("llama8b_decode", samples=48, select="pl")
+
+
+def test_full_size_llama3b_prefill_pl_sampled():
+    _full_size("llama3b_prefill", samples=48, select="pl")
+
+
+def test_full_size_qwen4b_prefill_sampled():
+    """The largest workload: 72 dictionaries x 131072 vectors in one step (a 16384-token
+    prefill; 9.4 M selection workgroups, 295 k screening workgroups)."""
+    _full_size("qwen4b_long_prefill", samples=48)
