@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="llama3b_decode")
     ap.add_argument("--select", default="gm", choices=["gm", "pl"])
     ap.add_argument("--warm", action="store_true", help="one dictionary set (cache-resident)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time decode-sized steps as eager launches instead of replaying one "
+                         "HIP graph per step (per-kernel times always come from an eager pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 3B prefill measurement added to the default decode line")
@@ -540,19 +543,20 @@ def measure_encode(args, name, steps, warmup):
     ws = fadkv.make_workspace(base_atoms, p, M)
     stream = torch.cuda.current_stream()
 
-    def step(k, ev=None):
+    def step(k, ev=None, strm=None):
+        st = stream if strm is None else strm
         A, U, X = sets[k % R], usages[k % R], batches[k % n_batches]
         if ev is not None:
-            ev[0].record(stream)
-        fadkv.fadkv_screen(A, X, p, out=pool, stream=stream)
+            ev[0].record(st)
+        fadkv.fadkv_screen(A, X, p, out=pool, stream=st)
         if ev is not None:
-            ev[1].record(stream)
-        fadkv.fadkv_select_support(A, X, p, pool, out=codes, stream=stream)
+            ev[1].record(st)
+        fadkv.fadkv_select_support(A, X, p, pool, out=codes, stream=st)
         if ev is not None:
-            ev[2].record(stream)
-        fadkv.fadkv_adapt(A, U, X, codes, p, replaced=replaced, workspace=ws, stream=stream)
+            ev[2].record(st)
+        fadkv.fadkv_adapt(A, U, X, codes, p, replaced=replaced, workspace=ws, stream=st)
         if ev is not None:
-            ev[3].record(stream)
+            ev[3].record(st)
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
@@ -565,6 +569,7 @@ def measure_encode(args, name, steps, warmup):
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
+    # per-kernel times: HIP events on the launch stream around every launch of the K steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -572,6 +577,31 @@ def measure_encode(args, name, steps, warmup):
         step(warmup + k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # whole-step throughput of decode-sized steps: the same K steps (same dictionary sets and
+    # batches, in the same order) replayed as one captured HIP graph each, so that the three
+    # launches of a step reach the GPU back to back
+    use_graph = not args.eager and T * M <= 65536
+    if use_graph:
+        combos = sorted({((warmup + k) % R, (warmup + k) % n_batches) for k in range(steps)})
+        graphs = {}
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for (ri, bi) in combos:
+                kk = next(k for k in range(R * n_batches) if (k % R, k % n_batches) == (ri, bi))
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(kk, strm=torch.cuda.current_stream())
+                graphs[(ri, bi)] = g
+        stream.wait_stream(side)
+        for g in graphs.values():
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            graphs[((warmup + k) % R, (warmup + k) % n_batches)].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     stage_ms = [0.0, 0.0, 0.0]
     for e in evs:
@@ -617,7 +647,8 @@ def measure_encode(args, name, steps, warmup):
         "config": {"workload": w.name, "num_dicts": T, "vectors_per_dict": M, "N": N, "n": w.n,
                    "s": w.s, "d": d, "select": args.select,
                    "dictionary_sets": R, "cache": "warm" if R == 1 else
-                   f"cold: {R} rotating dictionary sets ({R * dict_bytes / 2**20:.0f} MiB)"},
+                   f"cold: {R} rotating dictionary sets ({R * dict_bytes / 2**20:.0f} MiB)",
+                   "launch": "hip graph per step" if use_graph else "eager"},
         "roofline": roof,
         "kernels": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
