@@ -659,6 +659,59 @@ def measure_encode(args, name, steps, warmup):
     return w, out
 
 
+def yardsticks(dev):
+    """Measured references beside the published peaks: a plain device copy (bytes read +
+    written per second) and the library's bf16 GEMM of the 3B prefill score shape (per
+    dictionary 65536 x 128 times 128 x 4096, product written to HBM in bf16), timed over
+    chunks of 8 dictionaries with random operands."""
+    import torch
+
+    from sparse_dictionary_coding_amd import synth
+    out = {}
+    n = 1 << 28                                    # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    out["copy"] = {"gbs": 2 * n * 4 / (ms * 1e-3) / 1e9, "bytes_per_copy": 2 * n * 4,
+                   "what": "dst.copy_(src) of 1 GiB, read + write"}
+    del src, dst
+    w = synth.WORKLOADS["llama3b_prefill"]
+    T = 8
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    X = torch.randn(T, w.M, w.d, device=dev, dtype=torch.bfloat16, generator=g)
+    Dt = torch.randn(T, w.d, w.N, device=dev, dtype=torch.bfloat16, generator=g).contiguous()
+    prod = torch.empty(T, w.M, w.N, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        torch.bmm(X, Dt, out=prod)
+    torch.cuda.synchronize()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        torch.bmm(X, Dt, out=prod)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * T * w.M * w.N * w.d
+    out["gemm_bf16"] = {"tflops": flops / (ms * 1e-3) / 1e12,
+                        "ms_all_dictionaries": ms * w.num_dicts / T,
+                        "shape": f"{w.num_dicts} x ({w.M} x {w.d}) . ({w.d} x {w.N}), bf16 out",
+                        "what": "torch.bmm (the library GEMM), 8 dictionaries per call"}
+    del X, Dt, prod
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -689,6 +742,11 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
         out["prefill"]["screen_mfma"]["frac"] = out["prefill"]["screen_mfma"]["achieved"] / MFMA_BF16_PEAK_TFLOPS
         out["prefill"]["steps"], out["prefill"]["warmup"] = 3, 1
+        ys = yardsticks(torch.device("cuda:0"))
+        out["yardsticks"] = ys
+        out["screen_hbm"]["frac_of_copy"] = out["screen_hbm"]["achieved"] / ys["copy"]["gbs"]
+        out["prefill"]["screen_mfma"]["frac_of_gemm"] = (
+            out["prefill"]["screen_mfma"]["achieved"] / ys["gemm_bf16"]["tflops"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.select, args.cpu_seconds)
     print(json.dumps(out), flush=True)
