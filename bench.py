@@ -112,20 +112,32 @@ def cpu_baseline(w, select, seconds):
     rows_per_dict = min(w.M, 256)
     X = synth.to_f64(gen.batch(torch.from_numpy(A).to(synth.TORCH_DTYPES[w.dtype]),
                                M=rows_per_dict))
-    done = 0
-    dicts = 0
-    t0 = time.perf_counter()
-    for t in range(gen.T):
-        codes = oracle.encode(A[t:t + 1], X[t:t + 1], p, dict_ids=[t])
-        oracle.adapt(A[t:t + 1], np.zeros((1, w.N), np.int64), X[t:t + 1], codes, p, w.dtype)
-        done += rows_per_dict
-        dicts += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "vectors/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{dicts} of {w.num_dicts} dictionaries x {rows_per_dict} vectors "
-                      f"(encode + adapt, NumPy fp64), {dt:.1f} s"}
+    def run(budget):
+        done = 0
+        dicts = 0
+        t0 = time.perf_counter()
+        for t in range(gen.T):
+            codes = oracle.encode(A[t:t + 1], X[t:t + 1], p, dict_ids=[t])
+            oracle.adapt(A[t:t + 1], np.zeros((1, w.N), np.int64), X[t:t + 1], codes, p, w.dtype)
+            done += rows_per_dict
+            dicts += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return done, dicts, time.perf_counter() - t0
+
+    done, dicts, dt = run(seconds)
+    res = {"value": done / dt, "unit": "vectors/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{dicts} of {w.num_dicts} dictionaries x {rows_per_dict} vectors "
+                     f"(encode + adapt, NumPy fp64), {dt:.1f} s"}
+    try:   # the same oracle on one thread, on a quarter of the time budget
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, n1, t1 = run(seconds / 4)
+        res["single_thread"] = {"value": d1 / t1, "unit": "vectors/s", "cores": 1,
+                                "sample": f"{n1} dictionaries x {rows_per_dict} vectors, {t1:.1f} s"}
+    except ImportError:
+        pass
+    return res
 
 
 def bench_attend(args):
