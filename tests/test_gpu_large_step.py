@@ -20,7 +20,6 @@ from . import parity
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
 def _banner(msg):
@@ -67,6 +66,8 @@ CASES = [
     ("f16", 64, 3000, 256, 8, 2048, 2, False),      # head_dim 64
     ("f16", 128, 4096, 256, 8, 2080, 1, True),      # 3B dictionary shape
     ("bf16", 128, 8192, 512, 16, 2048, 1, True),    # 8B shape: boundary bins near the buffer size
+    ("f32", 64, 700, 32, 4, 2300, 1, False),        # fp32 dictionary (16x16x4 fp32 MFMA path)
+    ("bf16", 64, 2500, 128, 8, 2200, 2, True),      # bf16, head_dim 64
 ]
 
 
