@@ -236,6 +236,28 @@ def test_adapt_parity_usage_levels_and_exhaustion():
     assert np.all(rep == -1)
 
 
+def test_adapt_parity_at_the_3b_decode_shape():
+    """The commit of one 3B decode step at its real per-dictionary shape (N = 4096 fp16 atoms,
+    256 rows, s = 8, the synthetic 3B inputs with 20 % drifted rows) on four dictionaries (two
+    key, two value), from the oracle's codes: atoms, usage counters, replacements and rewritten
+    codes exactly as the oracle's.  Half the atoms start unused, so the drifted rows find slots;
+    the last dictionary has none left (every trigger exhausted)."""
+    _banner("adapt at the 3B decode shape")
+    w = synth.WORKLOADS["llama3b_decode"]
+    g = SyntheticKV(w, num_dicts=4)
+    A = g.atoms()
+    X = g.batch(A, step=2)
+    p = fadkv.Params(n=w.n, s=w.s)
+    rng = np.random.default_rng(8)
+    U = rng.integers(1, 4, size=(4, w.N)).astype(np.int64)
+    for t in range(3):
+        U[t, rng.permutation(w.N)[: w.N // 2]] = 0
+    oc = oracle.encode(to_f64(A), to_f64(X), parity.oracle_params(p))
+    rep, nu = _compare_adapt(A, X, U, oc, p, "f16")
+    trig = (oc.flags & FLAG_TRIGGER) != 0
+    assert np.sum(rep[:3] >= 0) > 0 and np.all(rep[3] == -1) and trig[3].any()
+
+
 def test_adapt_parity_both_commit_paths():
     """Steps of at most 4096 rows on dictionaries of at most 16384 atoms commit in one
     workgroup per dictionary, larger ones through separate mark / select / apply kernels (the
