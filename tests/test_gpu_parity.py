@@ -236,14 +236,16 @@ def test_adapt_parity_usage_levels_and_exhaustion():
     assert np.all(rep == -1)
 
 
-def test_adapt_parity_at_the_3b_decode_shape():
-    """The commit of one 3B decode step at its real per-dictionary shape (N = 4096 fp16 atoms,
-    256 rows, s = 8, the synthetic 3B inputs with 20 % drifted rows) on four dictionaries (two
-    key, two value), from the oracle's codes: atoms, usage counters, replacements and rewritten
-    codes exactly as the oracle's.  Half the atoms start unused, so the drifted rows find slots;
-    the last dictionary has none left (every trigger exhausted)."""
-    _banner("adapt at the 3B decode shape")
-    w = synth.WORKLOADS["llama3b_decode"]
+@pytest.mark.parametrize("name", ["llama3b_decode", "llama8b_decode", "qwen4b_long_decode"])
+def test_adapt_parity_at_decode_shapes(name):
+    """The commit of one decode step at its real per-dictionary shape (3B: N = 4096 fp16 atoms,
+    256 rows, s = 8; 8B: N = 8192, 512 rows, s = 16; Qwen3-4B: bf16, 128 rows; the synthetic
+    inputs with 20 % drifted rows) on four dictionaries (two key, two value), from the oracle's
+    codes: atoms, usage counters, replacements and rewritten codes exactly as the oracle's.  Half
+    the atoms start unused, so the drifted rows find slots; the last dictionary has none left
+    (every trigger exhausted)."""
+    _banner(f"adapt at the {name} shape")
+    w = synth.WORKLOADS[name]
     g = SyntheticKV(w, num_dicts=4)
     A = g.atoms()
     X = g.batch(A, step=2)
@@ -253,7 +255,7 @@ def test_adapt_parity_at_the_3b_decode_shape():
     for t in range(3):
         U[t, rng.permutation(w.N)[: w.N // 2]] = 0
     oc = oracle.encode(to_f64(A), to_f64(X), parity.oracle_params(p))
-    rep, nu = _compare_adapt(A, X, U, oc, p, "f16")
+    rep, nu = _compare_adapt(A, X, U, oc, p, w.dtype)
     trig = (oc.flags & FLAG_TRIGGER) != 0
     assert np.sum(rep[:3] >= 0) > 0 and np.all(rep[3] == -1) and trig[3].any()
 
