@@ -259,8 +259,8 @@ def encode_vector(D: np.ndarray, x: np.ndarray, p: OracleParams, delta: float) -
     coef[: len(S)] = c
     flags = FLAG_TRIGGER if e > delta else 0
     ties = (TIE_POOL if near_pool else 0) | (TIE_GREEDY if near_sel else 0)
-    if abs(e - delta) <= TIE_REL * delta:
-        ties |= TIE_DELTA
+    if np.isfinite(delta) and abs(e - delta) <= TIE_REL * delta:
+        ties |= TIE_DELTA      # an infinite delta is never approached: no near-tie there
     if ties:
         flags |= FLAG_NEAR_TIE
     return VectorCode(idx, coef, e, flags, ties, pool)
@@ -402,7 +402,8 @@ def append_dictionary(A: np.ndarray, usage: np.ndarray, X: np.ndarray, idx: np.n
                       coef: np.ndarray, relerr: np.ndarray, flags: np.ndarray, n_atoms: int,
                       p: OracleParams, dtype: str):
     """Commit one step by appending instead of reusing: the abstract contrasts FAD-KV with
-    "naive append-only" adaptation, whose dictionary grows during generation (Fig. 3a).
+    adaptation that only appends atoms, whose dictionary keeps growing during generation
+    (Fig. 3a).
 
     The dictionary is stored with capacity A.shape[0]; its first n_atoms rows are in use and
     the rest are zero (a zero atom scores 0 and is never selected).  Non-triggering rows commit
@@ -475,15 +476,27 @@ def reconstruct(atoms: np.ndarray, idx: np.ndarray, coef: np.ndarray) -> np.ndar
 # validation of a coder's choices at near-ties (used by parity tests)
 # ----------------------------------------------------------------------------------------
 
-def replay_support(D: np.ndarray, x: np.ndarray, S_given: Sequence[int], p: OracleParams):
+def replay_support(D: np.ndarray, x: np.ndarray, S_given: Sequence[int], p: OracleParams,
+                   pool: Optional[Sequence[int]] = None):
     """Check that a support chosen by another implementation is a valid answer.
 
     With a_n the n-th largest |sigma|, every valid pool holds the sure set
     {j : |sigma_j| > a_n (1 + TIE_REL)} and nothing outside the possible set
-    {j : |sigma_j| >= a_n (1 - TIE_REL)}.  Each given atom must be possible.  For GM each
-    given choice must reach (1 - TIE_REL) times the best |rho| over the not-yet-chosen sure
-    atoms at that step; for PL each given atom must reach (1 - TIE_REL) times the s-th largest
-    |sigma|.  Returns (valid, reason, c, e) with c and e computed on the given support.
+    {j : |sigma_j| >= a_n (1 - TIE_REL)}.  Each given atom must be possible.
+
+    Without ``pool``: for GM each given choice must reach (1 - TIE_REL) times the best |rho|
+    over the not-yet-chosen sure atoms at that step; for PL each given atom must reach
+    (1 - TIE_REL) times the s-th largest |sigma|.
+
+    With ``pool`` (the candidate pool the other implementation screened, n distinct atoms): the
+    pool must itself be a valid Top-n (n distinct possible atoms holding every sure atom), every
+    given atom must belong to it, and the choices are checked against that pool: for GM each
+    choice must reach (1 - TIE_REL) times the best |rho| over the pool atoms not yet chosen,
+    for PL each atom must reach (1 - TIE_REL) times the s-th largest |sigma| of the pool.  A
+    greedy that passed over a better atom of its own pool fails here even when that atom is
+    not in the sure set.
+
+    Returns (valid, reason, c, e) with c and e computed on the given support.
     """
     S_given = [int(j) for j in S_given if j >= 0]
     sigma = screening_scores(D, x)
@@ -499,8 +512,28 @@ def replay_support(D: np.ndarray, x: np.ndarray, S_given: Sequence[int], p: Orac
             return False, f"atom {j} outside every valid pool", None, None
     if len(set(S_given)) != len(S_given):
         return False, "repeated atom", None, None
+    if pool is not None:
+        P = [int(j) for j in pool]
+        Pset = set(P)
+        if len(Pset) != len(P) or len(P) != n_eff:
+            return False, f"pool of {len(P)} entries ({len(Pset)} distinct), not {n_eff}", None, None
+        outside = [j for j in P if j not in possible]
+        if outside:
+            return False, f"pool atom {outside[0]} outside every valid pool", None, None
+        missing = [int(j) for j in sure if int(j) not in Pset]
+        if missing:
+            return False, f"pool misses the sure atom {missing[0]}", None, None
+        for j in S_given:
+            if j not in Pset:
+                return False, f"atom {j} not in its own pool", None, None
+        candidates = np.array(sorted(Pset), dtype=np.int64)
+    else:
+        candidates = sure
     if p.select == "pl":
-        a_s = a[order[p.s - 1]]
+        if pool is not None:
+            a_s = np.sort(a[candidates])[::-1][p.s - 1]
+        else:
+            a_s = a[order[p.s - 1]]
         for j in S_given:
             if a[j] < a_s * (1 - TIE_REL):
                 return False, f"atom {j} not among the s largest", None, None
@@ -508,7 +541,7 @@ def replay_support(D: np.ndarray, x: np.ndarray, S_given: Sequence[int], p: Orac
         S: list[int] = []
         c = np.zeros(0)
         for j in S_given:
-            rest = np.array([i for i in sure if i not in S], dtype=np.int64)
+            rest = np.array([i for i in candidates if i not in S], dtype=np.int64)
             best = 0.0
             if rest.size:
                 rho = sigma[rest].copy()

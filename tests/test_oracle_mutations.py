@@ -88,6 +88,24 @@ MUTATIONS = {
         ("    for pv, sv in zip(P, S):", "    for pv, sv in zip(P[::-1], S):"),
     "PL takes the pool head unsorted":
         ("    S = [int(j) for j in pool[order[:s]]]", "    S = [int(j) for j in pool[::-1][:s]]"),
+    "greedy may re-pick a chosen atom":
+        ("        rest = np.array([j for j in pool if j not in S], dtype=np.int64)\n",
+         "        rest = np.array(list(pool), dtype=np.int64)\n"),
+    "greedy uses least-squares coefficients inside the loop":
+        ("        c = ridge_coefficients(D[S], sigma[S], ridge_abs, ridge_rel)\n    return S, c, near\n\n\ndef pl_support",
+         "        c = ridge_coefficients(D[S], sigma[S], 0.0, 0.0)\n"
+         "    c = ridge_coefficients(D[S], sigma[S], ridge_abs, ridge_rel)\n    return S, c, near\n\n\ndef pl_support"),
+    "replay skips the PL check":
+        ("            if a[j] < a_s * (1 - TIE_REL):\n", "            if False:\n"),
+    "replay checks picks against the sure set, not the given pool":
+        ("        candidates = np.array(sorted(Pset), dtype=np.int64)\n",
+         "        candidates = sure\n"),
+    "replay accepts a pick outside its own pool":
+        ("            if j not in Pset:\n", "            if False:\n"),
+    "replay accepts a pool without a sure atom":
+        ("        if missing:\n", "        if False:\n"),
+    "replay accepts a pool of the wrong size":
+        ("        if len(Pset) != len(P) or len(P) != n_eff:\n", "        if len(Pset) != len(P):\n"),
 }
 
 PIN_TESTS = [f for name, f in sorted(vars(pins).items())

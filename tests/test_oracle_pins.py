@@ -195,6 +195,41 @@ def test_gm_ties_go_to_lowest_index():
     assert list(pl.idx) == [1, 3]
 
 
+def test_gm_never_repicks_a_chosen_atom_by_hand():
+    """D = I (4 atoms), x = 3 e0 + 0.1 e1, s = 2.  Step 1 takes atom 0 with c0 = 3/1.2001.
+    At step 2 the chosen atom still correlates with the residual, rho_0 = 3 (1 - 1/1.2001)
+    = 0.50021, more than rho_1 = 0.1: a greedy that does not exclude chosen atoms takes atom 0
+    again.  Excluding it gives S = [0, 1], c = (3, 0.1)/1.2001 (G = I, so the ridge system is
+    diagonal)."""
+    D = np.eye(4)
+    x = np.array([3.0, 0.1, 0.0, 0.0])
+    vc = oracle.encode_vector(D, x, OracleParams(n=4, s=2), 0.5)
+    assert list(vc.idx) == [0, 1]
+    np.testing.assert_allclose(vc.coef, [3.0 / 1.2001, 0.1 / 1.2001], rtol=1e-13)
+    assert vc.ties == 0
+
+
+def test_gm_rho_uses_the_ridge_coefficients_by_hand():
+    """Three unit atoms d0 = e0, d1 = 0.9 e0 + sqrt(0.19) e1, d2 = e2 and x = (1, x1, 0.1) with
+    x1 = 0.05 / sqrt(0.19), so sigma = (1, 0.95, 0.1) and G_10 = 0.9, G_20 = 0.
+
+    Step 1 takes atom 0.  With the Table 5 ridge inside the greedy, c0 = 1/1.2001 and
+    rho_1 = 0.95 - 0.9/1.2001 = 0.20006 beats rho_2 = 0.1: S = [0, 1].  A greedy that uses
+    least-squares coefficients during the steps (c0 = 1) would see rho_1 = 0.05 < 0.1 and take
+    atom 2.  The final coefficients solve the 2x2 system [[1.2001, 0.9], [0.9, 1.2001]] c =
+    (1, 0.95), written out by Cramer's rule."""
+    r = np.sqrt(0.19)
+    D = np.array([[1.0, 0.0, 0.0], [0.9, r, 0.0], [0.0, 0.0, 1.0]])
+    x = np.array([1.0, 0.05 / r, 0.1])
+    vc = oracle.encode_vector(D, x, OracleParams(n=3, s=2), 0.5)
+    assert list(vc.idx) == [0, 1]
+    a, b, det = 1.2001, 0.9, 1.2001 ** 2 - 0.81
+    c_ref = [(a * 1.0 - b * 0.95) / det, (a * 0.95 - b * 1.0) / det]
+    np.testing.assert_allclose(vc.coef, c_ref, rtol=1e-12)
+    resid = x - c_ref[0] * D[0] - c_ref[1] * D[1]
+    assert vc.relerr == pytest.approx(np.linalg.norm(resid) / np.linalg.norm(x), rel=1e-12)
+
+
 def test_gm_orthonormal_closed_form():
     """Orthonormal D (G = I): S = the s largest |sigma| in order, c = sigma_S / 1.2001 and
     e^2 = (||x||^2 - ||sigma_S||^2 + (0.2001/1.2001)^2 ||sigma_S||^2) / ||x||^2."""
@@ -514,6 +549,8 @@ def test_adapt_delta_extremes():
     hi = oracle.encode(D, X, OracleParams(n=8, s=2, delta_key=np.inf))
     assert (lo.flags[0] & FLAG_TRIGGER).sum() == 9          # every non-zero row
     assert (hi.flags[0] & FLAG_TRIGGER).sum() == 0
+    # an infinite delta is never near: the trigger decision there is not a near-tie
+    assert not np.any(hi.ties & oracle.fadkv_oracle.TIE_DELTA)
 
 
 # ---------------------------------------------------------------------------------------
@@ -701,6 +738,56 @@ def test_replay_accepts_own_choices_and_rejects_a_swapped_atom():
             assert not oracle.replay_support(D, x, bad, p)[0], sel
             ok += 1
         assert ok >= 15
+
+
+def test_replay_pl_rejects_an_atom_outside_the_s_largest():
+    """D = I (8 atoms), x = (8, 7, ..., 1), n = 6, s = 3: PL must take {0, 1, 2}.  Atom 4 is in
+    every valid pool (|sigma| = 4 is the 5th largest) but not among the 3 largest, so a PL
+    support [0, 1, 4] is invalid; [2, 0, 1] (same set, any order) is valid."""
+    D = np.eye(8)
+    x = np.arange(8.0, 0.0, -1.0)
+    p = OracleParams(n=6, s=3, select="pl")
+    assert oracle.replay_support(D, x, [2, 0, 1], p)[0]
+    valid, why, _, _ = oracle.replay_support(D, x, [0, 1, 4], p)
+    assert not valid and "s largest" in why
+    assert not oracle.replay_support(D, x, [0, 1, 4], p, pool=[0, 1, 2, 3, 4, 5])[0]
+
+
+def _tie_at_pool_boundary():
+    """d0 = e0, d1 = e1, d2 = 0.6 e0 + 0.8 e2, d3 = e3 and x = (5, 1, -5, 2): sigma =
+    (5, 1, -1, 2) up to rounding of 0.6 and 0.8, so with n = 3 atoms 1 and 2 tie for the third
+    pool place (sure set {0, 3}).  GM takes atom 0 first (c0 = 5/1.2001); then
+    rho_1 = 1, rho_2 = -1 - 0.6 c0 = -3.4998, rho_3 = 2."""
+    D = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0], [0.6, 0, 0.8, 0], [0, 0, 0, 1.0]])
+    x = np.array([5.0, 1.0, -5.0, 2.0])
+    return D, x
+
+
+def test_replay_with_the_coder_pool():
+    """replay_support against the pool the coder screened.  With the tie above, pool {0, 2, 3}
+    is valid; inside it GM must take atom 2 at step 2 (|rho| 3.4998).  A coder that took
+    atom 3 (|rho| 2) passed over a better atom of its own pool: only the pool-aware check sees
+    that, since atom 2 is not in the sure set.  Pool {0, 1, 3} is valid too, and then [0, 3]
+    is right (atom 2 is not in that pool, rho_3 = 2 > rho_1 = 1); [0, 1] is a pick from
+    outside the pool {0, 2, 3}; a pool that leaves out the sure atom 3 or has the wrong size is
+    invalid."""
+    D, x = _tie_at_pool_boundary()
+    p = OracleParams(n=3, s=2)
+    sig = D @ x
+    assert abs(abs(sig[1]) - abs(sig[2])) <= 1e-12
+    assert oracle.replay_support(D, x, [0, 2], p, pool=[0, 2, 3])[0]
+    assert oracle.replay_support(D, x, [0, 3], p)[0]            # blind to the pool
+    valid, why, _, _ = oracle.replay_support(D, x, [0, 3], p, pool=[0, 2, 3])
+    assert not valid and "below best" in why
+    assert oracle.replay_support(D, x, [0, 3], p, pool=[0, 1, 3])[0]
+    valid, why, _, _ = oracle.replay_support(D, x, [0, 1], p, pool=[0, 2, 3])
+    assert not valid and "own pool" in why
+    assert not oracle.replay_support(D, x, [0, 2], p, pool=[0, 1, 2])[0]
+    assert not oracle.replay_support(D, x, [0, 2], p, pool=[0, 2, 3, 1])[0]
+    # PL inside the coder's pool: the two largest |sigma| of {0, 1, 3} are atoms 0 and 3
+    pl = OracleParams(n=3, s=2, select="pl")
+    assert oracle.replay_support(D, x, [0, 3], pl, pool=[0, 1, 3])[0]
+    assert not oracle.replay_support(D, x, [0, 1], pl, pool=[0, 1, 3])[0]
 
 
 def test_pool_recall_by_hand():
