@@ -624,15 +624,21 @@ def measure_encode(args, name, steps, warmup):
     vec_per_step = G
     value = vec_per_step * steps / wall
 
-    # algorithmic work per launch
+    # algorithmic work per launch (per-unit figures of the hot-path table, times the units)
+    code_bytes = G * (w.s * 8 + 5)                 # idx + coef per slot, relerr, flags
     screen_flops = 2.0 * N * d * G
-    screen_bytes = dict_bytes + G * d * esize + G * w.n * 6 + G
-    sel_cols = (w.s - 1) if args.select == "gm" else 0
-    sel_flops = 2.0 * G * (sel_cols * w.n * d + w.s * w.s * d / 2 + w.s * d)
-    adapt_bytes = G * (w.s * 8 + 5) + 2 * T * N * 4
+    screen_bytes = dict_bytes + G * d * esize      # the dictionary once + the vectors
+    # GM: 2 s n d flops per vector (a pool-wide Gram column per greedy step); the kernel skips
+    # the column of the last step, so it executes (s - 1) / s of that figure
+    sel_flops = 2.0 * G * w.s * w.n * d if args.select == "gm" else 2.0 * G * w.s * w.s * d
+    sel_flops_executed = (2.0 * G * (w.s - 1) * w.n * d if args.select == "gm"
+                          else 2.0 * G * w.s * w.s * d)
+    adapt_bytes = code_bytes + 2 * T * N * 4
+    step_bytes = dict_bytes + G * d * esize + code_bytes + 2 * T * N * 4
     kernels = {
         "screen_topn": {"ms": stage_ms[0], "flops": screen_flops, "bytes": screen_bytes},
-        "select_support": {"ms": stage_ms[1], "flops": sel_flops},
+        "select_support": {"ms": stage_ms[1], "flops": sel_flops,
+                           "flops_executed": sel_flops_executed},
         "adapt": {"ms": stage_ms[2], "bytes": adapt_bytes},
     }
     dominant = max(("screen_topn", "select_support"), key=lambda k: kernels[k]["ms"])
@@ -646,8 +652,9 @@ def measure_encode(args, name, steps, warmup):
         roof = {"kernel": "select_kernel", "bound": "alu", "achieved": ach,
                 "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / ALU_PEAK_TFLOPS,
                 "traffic": measured_traffic(w.name, args.select, "select_kernel")}
-    # the screening kernel against HBM as well (the decode-step figure of merit)
+    # the screening kernel against HBM, and the whole step (the decode-step figure of merit)
     screen_gbs = screen_bytes / (stage_ms[0] * 1e-3) / 1e9
+    step_gbs = step_bytes / (wall / steps) / 1e9
     trig = int((codes.flags & fadkv.FLAG_TRIGGER).ne(0).sum().item())
     rep = int((replaced >= 0).sum().item())
 
@@ -665,7 +672,11 @@ def measure_encode(args, name, steps, warmup):
         "kernels": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "screen_hbm": {"achieved": screen_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": screen_gbs / HBM_PEAK_GBS},
+                       "frac": screen_gbs / HBM_PEAK_GBS, "bytes": screen_bytes},
+        "step_hbm": {"achieved": step_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": step_gbs / HBM_PEAK_GBS, "bytes": step_bytes,
+                     "what": "dictionary + vectors + codes + usage read/write per step, over "
+                             "the whole step's time"},
         "last_step": {"triggers": trig, "replaced": rep},
     }
     return w, out
@@ -759,6 +770,13 @@ def main():
         out["screen_hbm"]["frac_of_copy"] = out["screen_hbm"]["achieved"] / ys["copy"]["gbs"]
         out["prefill"]["screen_mfma"]["frac_of_gemm"] = (
             out["prefill"]["screen_mfma"]["achieved"] / ys["gemm_bf16"]["tflops"])
+        # the other decode configurations, each a nested object of the same line
+        for other in ("llama8b_decode", "qwen4b_long_decode"):
+            torch.cuda.empty_cache()
+            _, o = measure_encode(args, other, args.steps, args.warmup)
+            out[other] = {k: o[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                             "roofline", "kernels", "screen_hbm", "step_hbm")}
+            out[other]["steps"], out[other]["warmup"] = args.steps, args.warmup
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.select, args.cpu_seconds)
     print(json.dumps(out), flush=True)

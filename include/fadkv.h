@@ -27,7 +27,8 @@
  *     (pool scores, Cholesky, residual) is fp32; new atoms are normalised in fp64 and rounded
  *     to the storage dtype (round to nearest even).
  *   - Limits.  d in {64, 128}; 1 <= N <= 65535; 1 <= s <= n <= min(N, 512); s <= 32;
- *     1 <= num_dicts; 0 <= M and num_dicts * M < 2^31.  atoms, X and X_hat must be 16-byte
+ *     1 <= num_dicts; 0 <= M and num_dicts * M < 2^31 (every accepted size runs: kernels whose
+ *     grid grows with the number of vectors are launched in chunks).  atoms, X and X_hat must be 16-byte
  *     aligned, the other arrays 4-byte aligned (flags: any alignment).
  *   - Streams.  Every call only enqueues work on `stream` (0 = the null stream) and never
  *     synchronises.  On one stream, encode of step t+1 sees adapt of step t.  Calls are
@@ -171,8 +172,8 @@ int fadkv_adapt(const fadkv_dict *dict, const fadkv_params *params, const void *
                 const fadkv_codes *codes, int32_t *replaced, void *workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
-/* Append-only growth: the contrast the abstract draws ("naive append-only strategies lead to
- * dictionary growth", Fig. 3a), offered to measure it.  Same as fadkv_adapt except where a
+/* Append-only growth: the contrast the abstract draws (an adaptive dictionary that only ever
+ * appends keeps growing during generation; FAD-KV, abstract and Fig. 3a), offered to measure it.  Same as fadkv_adapt except where a
  * triggering row's new atom goes: dictionary t uses slots [0, n_atoms[t]) of its capacity N
  * (dict->N; unused slots must hold zeros: they score 0 and are never selected), and its k-th
  * triggering row (row order) writes round(x/||x||) to slot n_atoms[t] + k while slots remain,
@@ -210,12 +211,14 @@ int fadkv_reconstruct(const fadkv_dict *dict, const int32_t *idx, const float *c
  *                 share row r's keys and values (1 <= G <= 64)
  *   out           device fp32 [R][G][d], overwritten
  *   scale         finite (e.g. 1/sqrt(d))
- * 1 <= s <= 32, N <= 16384, R >= 0, T >= 0, R*G < 2^31.  Workspace: at least
- * fadkv_attend_workspace_bytes() bytes, 256-byte aligned, caller-owned (it holds q . D_K^T,
- * then the atom weights, fp32 [R*G][N], and partial outputs per range of 128 atoms, fp32
- * [ceil(N/128)][R*G][d]).  Checked synchronously; nothing is launched on error.  fp32
- * throughout after the 16-bit products; the value weights are accumulated with LDS atomics,
- * so the last bits of out may differ between runs. */
+ * 1 <= s <= 32, N <= 16384, 0 <= R <= 2^22, T >= 0, R*G <= 2^24 (the kernels' grids).
+ * Workspace: at least fadkv_attend_workspace_bytes() bytes, 256-byte aligned, caller-owned (it
+ * holds q . D_K^T, then the atom weights, fp32 [R*G][N], and partial outputs per range of 128
+ * atoms, fp32 [ceil(N/128)][R*G][d]).  Checked synchronously; nothing is launched on error.
+ * fp32 throughout after the 16-bit products.  Determinism: for N <= 13311 the value weights
+ * are accumulated exactly as 64-bit fixed point, so out is bitwise reproducible; for larger N
+ * they are accumulated with fp32 LDS atomics, whose order varies, so the last bits of out may
+ * differ between runs. */
 int fadkv_attend_workspace_bytes(const fadkv_dict *dict, int64_t R, int32_t G, size_t *bytes);
 int fadkv_attend(const fadkv_dict *dict, int32_t layer, int32_t s, const int32_t *k_idx,
                  const float *k_coef, const int32_t *v_idx, const float *v_coef,

@@ -30,8 +30,8 @@ __global__ __launch_bounds__(256) void adapt_mark_kernel(const int32_t *__restri
                                                          uint32_t *__restrict__ usage,
                                                          uint8_t *__restrict__ touched,
                                                          int touched_stride, int N, int M, int s,
-                                                         size_t G) {
-  const size_t gv = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                                         size_t G, size_t base) {
+  const size_t gv = base + (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gv >= G) return;
   const int dict = (int)(gv / (size_t)M);
   const uint8_t fl = flags[gv];
@@ -235,10 +235,10 @@ __global__ __launch_bounds__(256) void adapt_apply_kernel(
     int M, int s, float ridge_abs, float ridge_rel, const int32_t *__restrict__ rank,
     const int32_t *__restrict__ cand, const int32_t *__restrict__ ccount, int32_t *__restrict__ idx,
     float *__restrict__ coef, float *__restrict__ relerr, uint8_t *__restrict__ flags,
-    int32_t *__restrict__ replaced, size_t G) {
+    int32_t *__restrict__ replaced, size_t G, size_t base) {
   constexpr int ROWB = D * Elem<DT>::bytes;
   const int lane = threadIdx.x & 63;
-  const size_t gv = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t gv = base + (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gv >= G) return;
   const int dict = (int)(gv / (size_t)M);
   const int r = rank[gv];
@@ -397,9 +397,9 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const uint8_t *__restr
                                                           const int32_t *__restrict__ idx,
                                                           const float *__restrict__ coef, int N,
                                                           int M, int s, uint8_t *__restrict__ out,
-                                                          size_t G) {
+                                                          size_t G, size_t base) {
   constexpr int ROWB = D * Elem<DT>::bytes;
-  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t e = base + (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t gv = e / D;
   const int i = (int)(e % D);
   if (gv >= G) return;
@@ -448,19 +448,28 @@ hipError_t launch_adapt(int dtype, int d, void *atoms, uint32_t *usage, const vo
                        dim3(MARK_THREADS), lds, stream, idx, flags, usage, touched, touched_stride,
                        N, M, s, chunks);
   } else {
-    hipLaunchKernelGGL(adapt_mark_kernel, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, stream,
-                       idx, flags, usage, touched, touched_stride, N, M, s, G);
+    const size_t blocks = (G + 255) / 256;
+    for (size_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+      const size_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+      hipLaunchKernelGGL(adapt_mark_kernel, dim3((unsigned)nb), dim3(256), 0, stream, idx, flags,
+                         usage, touched, touched_stride, N, M, s, G, b0 * 256);
+    }
   }
   hipLaunchKernelGGL(adapt_select_kernel, dim3(num_dicts), dim3(SEL_THREADS), 0, stream, usage,
                      touched, touched_stride, flags, N, M, tau_c, rank, cand, ccount, n_atoms);
-  dim3 grid((unsigned)((G + 3) / 4)), block(256);
+  const size_t blocks = (G + 3) / 4;
+  for (size_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    const dim3 grid((unsigned)nb), block(256);
 #define L(DT, D)                                                                                   \
   hipLaunchKernelGGL((adapt_apply_kernel<DT, D>), grid, block, 0, stream, A, usage, Xb, N, M, s,  \
-                     ridge_abs, ridge_rel, rank, cand, ccount, idx, coef, relerr, flags, replaced, G)
-  if (dtype == DT_F32) { if (d == 64) L(DT_F32, 64); else L(DT_F32, 128); }
-  else if (dtype == DT_F16) { if (d == 64) L(DT_F16, 64); else L(DT_F16, 128); }
-  else { if (d == 64) L(DT_BF16, 64); else L(DT_BF16, 128); }
+                     ridge_abs, ridge_rel, rank, cand, ccount, idx, coef, relerr, flags, replaced, G, \
+                     b0 * 4)
+    if (dtype == DT_F32) { if (d == 64) L(DT_F32, 64); else L(DT_F32, 128); }
+    else if (dtype == DT_F16) { if (d == 64) L(DT_F16, 64); else L(DT_F16, 128); }
+    else { if (d == 64) L(DT_BF16, 64); else L(DT_BF16, 128); }
 #undef L
+  }
   return hipGetLastError();
 }
 
@@ -469,19 +478,23 @@ hipError_t launch_reconstruct(int dtype, int d, const void *atoms, const int32_t
                               int out_dtype, hipStream_t stream) {
   const size_t G = (size_t)num_dicts * M;
   const size_t E = G * d;
-  dim3 grid((unsigned)((E + 255) / 256)), block(256);
+  const size_t blocks = (E + 255) / 256;
   const uint8_t *A = static_cast<const uint8_t *>(atoms);
   uint8_t *O = static_cast<uint8_t *>(out);
+  for (size_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    const dim3 grid((unsigned)nb), block(256);
 #define L(DT, D, ODT) \
-  hipLaunchKernelGGL((reconstruct_kernel<DT, D, ODT>), grid, block, 0, stream, A, idx, coef, N, M, s, O, G)
+  hipLaunchKernelGGL((reconstruct_kernel<DT, D, ODT>), grid, block, 0, stream, A, idx, coef, N, M, s, O, G, b0 * 256)
 #define LO(DT, D) do { if (out_dtype == DT_F32) L(DT, D, DT_F32); else if (out_dtype == DT_F16) L(DT, D, DT_F16); else L(DT, D, DT_BF16); } while (0)
 #define LD(DT) do { if (d == 64) LO(DT, 64); else LO(DT, 128); } while (0)
-  if (dtype == DT_F32) LD(DT_F32);
-  else if (dtype == DT_F16) LD(DT_F16);
-  else LD(DT_BF16);
+    if (dtype == DT_F32) LD(DT_F32);
+    else if (dtype == DT_F16) LD(DT_F16);
+    else LD(DT_BF16);
 #undef LD
 #undef LO
 #undef L
+  }
   return hipGetLastError();
 }
 

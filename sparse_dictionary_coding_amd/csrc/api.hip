@@ -13,6 +13,9 @@ constexpr int kMaxN = 65535;    // pool indices are stored as uint16
 constexpr int kMaxPool = 512;   // one selection thread per pool entry
 constexpr int kMaxS = 32;
 constexpr int kMaxAttendN = 16384;   // a query's q . D_K^T row and atom weights live in LDS
+// the attention kernels' grids: one 1024-thread workgroup per row, d threads per query output
+constexpr int64_t kMaxAttendR = int64_t(1) << 22;
+constexpr int64_t kMaxAttendRG = int64_t(1) << 24;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -345,7 +348,7 @@ int fadkv_attend_workspace_bytes(const fadkv_dict *dict, int64_t R, int32_t G, s
       (dict->d != 64 && dict->d != 128))
     return FADKV_ERR_SHAPE;
   if (R < 0 || G < 1 || G > 64) return FADKV_ERR_SHAPE;
-  if ((double)R * (double)G >= 2147483648.0) return FADKV_ERR_SHAPE;
+  if (R > kMaxAttendR || (double)R * (double)G > (double)kMaxAttendRG) return FADKV_ERR_SHAPE;
   *bytes = attend_ws_bytes(dict, R, G);
   return FADKV_OK;
 }
@@ -359,7 +362,7 @@ int fadkv_attend(const fadkv_dict *dict, int32_t layer, int32_t s, const int32_t
   if (dict->N > kMaxAttendN) return FADKV_ERR_SHAPE;
   if (layer < 0 || 2 * (int64_t)layer + 1 >= dict->num_dicts) return FADKV_ERR_SHAPE;
   if (s < 1 || s > kMaxS || R < 0 || T < 0 || G < 1 || G > 64) return FADKV_ERR_SHAPE;
-  if ((double)R * (double)G >= 2147483648.0) return FADKV_ERR_SHAPE;
+  if (R > kMaxAttendR || (double)R * (double)G > (double)kMaxAttendRG) return FADKV_ERR_SHAPE;
   if ((double)R * (double)T * (double)s >= 9.0e18) return FADKV_ERR_SHAPE;
   if (!isfinite(scale)) return FADKV_ERR_ARG;
   if (R == 0) return FADKV_OK;

@@ -8,6 +8,11 @@ namespace fadkv {
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
+// A dispatch counts work-items in 32 bits per grid dimension, so launches whose grid grows with
+// the number of vectors are issued in chunks of at most 2^22 workgroups (2^31 work-items at 512
+// threads); each chunk passes its first unit as `base`.
+constexpr size_t kMaxBlocksPerLaunch = size_t(1) << 22;
+
 // vector-status byte written by the screening kernel for the selection kernel
 enum { VS_NORMAL = 0, VS_ZERO = 1, VS_NONFINITE = 2 };
 

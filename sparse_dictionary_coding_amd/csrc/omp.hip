@@ -101,11 +101,11 @@ __global__ __launch_bounds__(256) void omp_init_kernel(const uint8_t *__restrict
                                                        int32_t *__restrict__ idx,
                                                        float *__restrict__ coef,
                                                        float *__restrict__ relerr,
-                                                       uint8_t *__restrict__ flags) {
+                                                       uint8_t *__restrict__ flags, size_t base) {
   constexpr int ROWB = D * Elem<DT>::bytes;
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
-  const size_t gv = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t gv = base + (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gv >= G) return;
   const uint8_t *xr = X + gv * ROWB;
   float ss = 0.f;
@@ -266,12 +266,12 @@ __global__ __launch_bounds__(256) void omp_update_kernel(
     uint8_t *__restrict__ status, const int32_t *__restrict__ jstar,
     int32_t *__restrict__ S, float *__restrict__ Lm, float *__restrict__ sig,
     uint8_t *__restrict__ R, int32_t *__restrict__ idx, float *__restrict__ coef,
-    float *__restrict__ relerr, uint8_t *__restrict__ flags) {
+    float *__restrict__ relerr, uint8_t *__restrict__ flags, size_t base) {
   constexpr int ROWB = D * Elem<DT>::bytes;
   constexpr int PER = D / 64;
   constexpr int NP = Parts<DT>::n;
   const int lane = threadIdx.x & 63;
-  const size_t gv = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t gv = base + (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gv >= G) return;
   if (status[gv] != VS_NORMAL) return;
   const int dict = (int)(gv / (size_t)M);
@@ -436,11 +436,15 @@ namespace {
 template <int DT, int D, int SMAX>
 void launch_update(const OmpArgs &a, int k, hipStream_t stream) {
   const size_t G = (size_t)a.num_dicts * a.M;
-  hipLaunchKernelGGL((omp_update_kernel<DT, D, SMAX>), dim3((unsigned)((G + 3) / 4)), dim3(256), 0,
-                     stream, static_cast<const uint8_t *>(a.atoms),
-                     static_cast<const uint8_t *>(a.X), a.N, a.M, G, a.s, k, a.ridge_abs,
-                     a.ridge_rel, a.delta_key, a.delta_value, a.status, a.jstar, a.S, a.L, a.sig,
-                     a.R, a.idx, a.coef, a.relerr, a.flags);
+  const size_t blocks = (G + 3) / 4;
+  for (size_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    hipLaunchKernelGGL((omp_update_kernel<DT, D, SMAX>), dim3((unsigned)nb), dim3(256), 0,
+                       stream, static_cast<const uint8_t *>(a.atoms),
+                       static_cast<const uint8_t *>(a.X), a.N, a.M, G, a.s, k, a.ridge_abs,
+                       a.ridge_rel, a.delta_key, a.delta_value, a.status, a.jstar, a.S, a.L,
+                       a.sig, a.R, a.idx, a.coef, a.relerr, a.flags, b0 * 4);
+  }
 }
 
 template <int DT, int D>
@@ -448,8 +452,12 @@ hipError_t run(const OmpArgs &a, hipStream_t stream) {
   const size_t G = (size_t)a.num_dicts * a.M;
   const uint8_t *A = static_cast<const uint8_t *>(a.atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(a.X);
-  hipLaunchKernelGGL((omp_init_kernel<DT, D>), dim3((unsigned)((G + 3) / 4)), dim3(256), 0, stream,
-                     Xb, G, a.s, a.status, a.idx, a.coef, a.relerr, a.flags);
+  const size_t blocks = (G + 3) / 4;
+  for (size_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    hipLaunchKernelGGL((omp_init_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, stream, Xb, G,
+                       a.s, a.status, a.idx, a.coef, a.relerr, a.flags, b0 * 4);
+  }
   const int nvb = (a.M + CVT - 1) / CVT;
   const dim3 cgrid((unsigned)(8 * ((a.num_dicts + 7) / 8) * nvb));
   for (int k = 0; k < a.s; ++k) {

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
     int n, int s, float ridge_abs, float ridge_rel, float delta_key, float delta_value,
     const uint16_t *__restrict__ pool_idx, const float *__restrict__ pool_sig,
     const uint8_t *__restrict__ vstat, int32_t *__restrict__ out_idx, float *__restrict__ out_coef,
-    float *__restrict__ out_relerr, uint8_t *__restrict__ out_flags) {
+    float *__restrict__ out_relerr, uint8_t *__restrict__ out_flags, unsigned base) {
   constexpr int NW = RowWords<DT, D>::NW;
   constexpr int ROWB = RowWords<DT, D>::ROWB;
   constexpr int PUB = SMAX + 2;   // published slot: W row, score, squared norm
@@ -107,8 +107,9 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
   // With a multiple of 8 dictionaries, workgroup i (dispatched to XCD i % 8) takes a vector of
   // dictionary xcd + 8 * (r / M), r = i / 8: each dictionary's pool rows are gathered through
   // one XCD's L2.
-  // (32-bit arithmetic: the grid has num_dicts * M < 2^32 workgroups)
-  const unsigned bid = blockIdx.x, uM = (unsigned)M;
+  // (32-bit arithmetic: num_dicts * M < 2^31 workgroups over all chunks; base is a multiple of
+  // 8, so the XCD of workgroup bid is still bid % 8)
+  const unsigned bid = base + blockIdx.x, uM = (unsigned)M;
   unsigned dict_u, vec_u;
   if ((num_dicts & 7) == 0) {
     const unsigned r = bid / 8u;
@@ -309,7 +310,8 @@ __global__ __launch_bounds__(MAXW * 64, (DT != DT_F32 && SMAX <= 16) ? 4 : 1) vo
 #define FADKV_SEL_INST(DT, D, SM, MW)                                                             \
   template __global__ void select_kernel<DT, D, SM, MW>(                                         \
       const uint8_t *, const uint8_t *, int, int, int, int, int, float, float, float, float,      \
-      const uint16_t *, const float *, const uint8_t *, int32_t *, float *, float *, uint8_t *);
+      const uint16_t *, const float *, const uint8_t *, int32_t *, float *, float *, uint8_t *,  \
+      unsigned);
 #define FADKV_SEL_INST_S(DT, D, SM) FADKV_SEL_INST(DT, D, SM, 4) FADKV_SEL_INST(DT, D, SM, 8)
 #define FADKV_SEL_INST_D(DT, D) \
   FADKV_SEL_INST_S(DT, D, 8) FADKV_SEL_INST_S(DT, D, 16) FADKV_SEL_INST_S(DT, D, 32)
@@ -327,24 +329,27 @@ hipError_t launch_select(int dtype, int d, const void *atoms, const void *X, int
                          float *relerr, uint8_t *flags, hipStream_t stream) {
   const size_t G = (size_t)num_dicts * M;
   const unsigned threads = (unsigned)(((n + 63) / 64) * 64);   // n <= 512: at most 8 waves
-  dim3 grid((unsigned)G), block(threads);
   const uint8_t *A = static_cast<const uint8_t *>(atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
+  for (size_t b0 = 0; b0 < G; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = G - b0 < kMaxBlocksPerLaunch ? G - b0 : kMaxBlocksPerLaunch;
+    const dim3 grid((unsigned)nb), block(threads);
 #define L(DT, D, SM, MW)                                                                          \
   hipLaunchKernelGGL((select_kernel<DT, D, SM, MW>), grid, block, 0, stream, A, Xb, num_dicts, N, \
                      M, n, s, ridge_abs, ridge_rel, delta_key, delta_value, pool_idx,              \
-                     pool_sig, vstat, idx, coef, relerr, flags)
+                     pool_sig, vstat, idx, coef, relerr, flags, (unsigned)b0)
 #define LW(DT, D, SM) do { if (threads <= 256) L(DT, D, SM, 4); else L(DT, D, SM, 8); } while (0)
 #define LS(DT, D) \
   do { if (s <= 8) LW(DT, D, 8); else if (s <= 16) LW(DT, D, 16); else LW(DT, D, 32); } while (0)
 #define LD(DT) do { if (d == 64) LS(DT, 64); else LS(DT, 128); } while (0)
-  if (dtype == DT_F32) LD(DT_F32);
-  else if (dtype == DT_F16) LD(DT_F16);
-  else LD(DT_BF16);
+    if (dtype == DT_F32) LD(DT_F32);
+    else if (dtype == DT_F16) LD(DT_F16);
+    else LD(DT_BF16);
 #undef LD
 #undef LS
 #undef LW
 #undef L
+  }
   return hipGetLastError();
 }
 

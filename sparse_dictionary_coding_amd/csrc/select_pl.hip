@@ -51,12 +51,12 @@ __global__ __launch_bounds__(PL_WAVES * 64) void select_pl_kernel(
     const uint16_t *__restrict__ pool_idx, const float *__restrict__ pool_sig,
     const uint8_t *__restrict__ vstat, int32_t *__restrict__ out_idx,
     float *__restrict__ out_coef, float *__restrict__ out_relerr,
-    uint8_t *__restrict__ out_flags) {
+    uint8_t *__restrict__ out_flags, size_t base) {
   constexpr int ROWB = D * Elem<DT>::bytes;
   constexpr int PER = D / 64;
   __shared__ float s_G[PL_WAVES][SMAX * SMAX];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const size_t gv = (size_t)blockIdx.x * PL_WAVES + wave;
+  const size_t gv = base + (size_t)blockIdx.x * PL_WAVES + wave;
   if (gv >= G) return;
   const int dict = (int)(gv / (size_t)M);
   const uint8_t st = vstat[gv];
@@ -239,21 +239,25 @@ hipError_t launch_select_pl(int dtype, int d, const void *atoms, const void *X, 
                             const float *pool_sig, const uint8_t *vstat, int32_t *idx,
                             float *coef, float *relerr, uint8_t *flags, hipStream_t stream) {
   const size_t G = (size_t)num_dicts * M;
-  const dim3 grid((unsigned)((G + PL_WAVES - 1) / PL_WAVES)), block(PL_WAVES * 64);
+  const size_t blocks = (G + PL_WAVES - 1) / PL_WAVES;
   const uint8_t *A = static_cast<const uint8_t *>(atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
+  for (size_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    const dim3 grid((unsigned)nb), block(PL_WAVES * 64);
 #define L(DT, D, SM)                                                                              \
   hipLaunchKernelGGL((select_pl_kernel<DT, D, SM>), grid, block, 0, stream, A, Xb, N, M, G, n, s, \
                      ridge_abs, ridge_rel, delta_key, delta_value, pool_idx, pool_sig, vstat, idx, \
-                     coef, relerr, flags)
+                     coef, relerr, flags, b0 * PL_WAVES)
 #define LS(DT, D) do { if (s <= 8) L(DT, D, 8); else if (s <= 16) L(DT, D, 16); else L(DT, D, 32); } while (0)
 #define LD(DT) do { if (d == 64) LS(DT, 64); else LS(DT, 128); } while (0)
-  if (dtype == DT_F32) LD(DT_F32);
-  else if (dtype == DT_F16) LD(DT_F16);
-  else LD(DT_BF16);
+    if (dtype == DT_F32) LD(DT_F32);
+    else if (dtype == DT_F16) LD(DT_F16);
+    else LD(DT_BF16);
 #undef LD
 #undef LS
 #undef L
+  }
   return hipGetLastError();
 }
 

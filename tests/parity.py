@@ -77,7 +77,10 @@ def _close(a, b, rtol):
 
 
 def compare_vector(rep: Report, where: str, D, x, gi, gc, ge, gf, oc: oracle.VectorCode,
-                   p: OracleParams, delta: float):
+                   p: OracleParams, delta: float, pool=None):
+    """Compare one vector's GPU code with the oracle's.  ``pool``, when given, is the candidate
+    pool the GPU screened for this vector: a near-tie choice is then replayed inside that pool
+    (the pool must itself be a valid Top-n, and every greedy pick the best of its own pool)."""
     rep.vectors += 1
     if oc.flags & FLAG_NONFINITE:
         rep.nonfinite += 1
@@ -97,7 +100,7 @@ def compare_vector(rep: Report, where: str, D, x, gi, gc, ge, gf, oc: oracle.Vec
             rep.failures.append(f"{where}: trigger {gf & 1} vs {oc.flags & 1}")
         return
     rep.near_tie += 1
-    valid, why, c, e = oracle.replay_support(D, x, gi, p)
+    valid, why, c, e = oracle.replay_support(D, x, gi, p, pool=pool)
     if not valid:
         rep.failures.append(f"{where}: near-tie choice invalid: {why}")
         return
@@ -113,10 +116,12 @@ def compare_vector(rep: Report, where: str, D, x, gi, gc, ge, gf, oc: oracle.Vec
 
 
 def compare_encode(atoms_f64, X_f64, gpu, p: OracleParams, rows=None, dict_ids=None,
-                   oracle_codes: oracle.Codes | None = None) -> tuple[Report, oracle.Codes]:
+                   oracle_codes: oracle.Codes | None = None,
+                   pools=None) -> tuple[Report, oracle.Codes]:
     """Compare GPU codes (numpy tuple) with the oracle on every (or the listed) rows.
 
-    rows: iterable of (t, m); dict_ids gives the dictionary number of slice t (delta parity).
+    rows: iterable of (t, m); dict_ids gives the dictionary number of slice t (delta parity);
+    pools: the GPU's candidate pools [T][M][n] (pool_from_workspace), used at near-ties.
     Returns the report and the oracle's codes for all compared rows (full arrays when rows is
     None).
     """
@@ -136,7 +141,8 @@ def compare_encode(atoms_f64, X_f64, gpu, p: OracleParams, rows=None, dict_ids=N
         else:
             oc = oracle.encode_vector(atoms_f64[t], X_f64[t, m], p, delta)
         compare_vector(rep, f"dict {t} row {m}", atoms_f64[t], X_f64[t, m], gi[t, m], gc[t, m],
-                       ge[t, m], int(gf[t, m]), oc, p, delta)
+                       ge[t, m], int(gf[t, m]), oc, p, delta,
+                       pool=None if pools is None else pools[t, m])
     return rep, oracle_codes
 
 
@@ -157,5 +163,41 @@ def pool_from_workspace(ws: torch.Tensor, T: int, M: int, n: int):
     return idx.reshape(T, M, n), sig.reshape(T, M, n)
 
 
+def pool_rows_from_workspace(ws: torch.Tensor, T: int, M: int, n: int, rows):
+    """The GPU's candidate pools of the listed rows (t, m) only, from the workspace head (see
+    pool_from_workspace), as {(t, m): int64 atom indices}."""
+    idx = ws[: T * M * n * 2].view(torch.int16).view(T, M, n)
+    return {(t, m): idx[t, m].to(torch.int64).cpu().numpy() & 0xFFFF for (t, m) in rows}
+
+
 def to_host(t: torch.Tensor) -> np.ndarray:
     return to_f64(t)
+
+
+def gpu_codes_as_oracle(gi, gc, ge, gf) -> oracle.Codes:
+    """The GPU's codes (numpy arrays from codes_to_numpy) as oracle Codes, so that the oracle
+    can commit exactly the supports and trigger bits the GPU produced."""
+    return oracle.Codes(np.array(gi, np.int32, copy=True), np.array(gc, np.float64, copy=True),
+                        np.array(ge, np.float64, copy=True), np.array(gf, np.uint8, copy=True),
+                        np.zeros(np.shape(gf), np.uint8))
+
+
+def check_commit(where: str, A_before, U_before, X, gpu_before, op: OracleParams, dtype: str,
+                 A_after, U_after, replaced, gpu_after):
+    """The adaptation commit of one step, exactly: the oracle commits the GPU's own codes
+    (supports and trigger bits as the GPU encoded them) from the GPU's step-start atoms and
+    usage; the GPU's replacements, usage counters, new atoms and rewritten codes must equal the
+    oracle's.  Adaptation reads nothing else of the codes, so this holds whatever near-ties the
+    encode met.  Returns (number of replacements, number of exhausted rows)."""
+    oc = gpu_codes_as_oracle(*gpu_before)
+    na, nu, ncodes, orep = oracle.adapt(A_before, U_before, X, oc, op, dtype)
+    gi, gc, ge, gf = gpu_after
+    assert np.array_equal(replaced, orep), f"{where}: replacements differ"
+    assert np.array_equal(np.asarray(U_after, np.int64), nu), f"{where}: usage counters differ"
+    assert np.array_equal(A_after, na), f"{where}: new atoms differ"
+    assert np.array_equal(gi, ncodes.idx), f"{where}: rewritten code indices differ"
+    assert np.array_equal(gf, ncodes.flags), f"{where}: flags differ"
+    np.testing.assert_allclose(gc, ncodes.coef, rtol=1e-6, atol=1e-7, err_msg=where)
+    np.testing.assert_allclose(ge, ncodes.relerr, rtol=1e-6, atol=1e-7, err_msg=where)
+    from oracle.fadkv_oracle import FLAG_EXHAUSTED
+    return int(np.sum(orep >= 0)), int(np.sum((ncodes.flags & FLAG_EXHAUSTED) != 0))

@@ -228,3 +228,25 @@ def test_attend_workspace_size():
     assert out.value >= 256 * 3 * 4096 * 4 and out.value % 256 == 0
     assert L.fadkv_attend_workspace_bytes(ctypes.byref(_dict(num_dicts=1)), 1, 1,
                                           ctypes.byref(out)) == -3
+
+
+def test_size_limits_at_the_boundary():
+    """The vector-count limit num_dicts * M < 2^31 is accepted right up to the boundary (the
+    kernels whose grids grow with it are launched in chunks) and rejected at it; attention takes
+    R <= 2^22 rows and R * G <= 2^24 queries, its grids' limits."""
+    L = fadkv.lib()
+    assert _ws(_dict(num_dicts=2, N=1024), _params(n=64, s=8), (1 << 30) - 1)[0] == 0
+    assert _ws(_dict(num_dicts=2, N=1024), _params(n=64, s=8), 1 << 30)[0] == -3
+    assert _ws(_dict(num_dicts=1, N=1024), _params(n=512, s=8), (1 << 31) - 1)[0] == 0
+    out = ctypes.c_size_t(0)
+    ws = lambda R, G: L.fadkv_attend_workspace_bytes(ctypes.byref(_dict(num_dicts=2, N=64)), R, G,
+                                                     ctypes.byref(out))
+    assert ws(1 << 22, 4) == 0 and ws((1 << 22) + 1, 1) == -3
+    assert ws(1 << 18, 64) == 0 and ws(1 << 18, 65) == -3 and ws((1 << 18) + 1, 64) == -3
+
+    def att(R, G):
+        return L.fadkv_attend(ctypes.byref(_dict(num_dicts=2, N=64)), 0, 8, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, R, 10, FAKE, G, 0.1, FAKE, FAKE, 16, None)
+    assert att((1 << 22) + 1, 1) == -3 and att((1 << 18) + 1, 64) == -3
+    assert att(1 << 18, 64) == -4        # accepted shape; only the tiny workspace is refused
+

@@ -46,9 +46,11 @@ def test_tiny_workload_encode_parity(select):
     _banner(f"tiny workload {select}")
     _, A, X = make(w)
     p = fadkv.Params(n=w.n, s=w.s, select=select)
-    codes = parity.gpu_encode(A.to(DEV), X.to(DEV), p)
+    ws = fadkv.make_workspace(A.to(DEV), p, w.M)
+    codes = parity.gpu_encode(A.to(DEV), X.to(DEV), p, workspace=ws)
+    pools, _ = parity.pool_from_workspace(ws, 1, w.M, w.n)
     rep, _ = parity.compare_encode(to_f64(A), to_f64(X), parity.codes_to_numpy(codes),
-                                   parity.oracle_params(p))
+                                   parity.oracle_params(p), pools=pools)
     rep.check()
     assert rep.exact >= 0.9 * rep.vectors
 
@@ -79,11 +81,12 @@ def test_encode_parity_shapes(shape, select):
     ws = fadkv.make_workspace(A.to(DEV), p, M)
     codes = parity.gpu_encode(A.to(DEV), X.to(DEV), p, workspace=ws)
     op = parity.oracle_params(p)
-    rep, oc = parity.compare_encode(to_f64(A), to_f64(X), parity.codes_to_numpy(codes), op)
+    pidx, psig = parity.pool_from_workspace(ws, T, M, n)
+    rep, oc = parity.compare_encode(to_f64(A), to_f64(X), parity.codes_to_numpy(codes), op,
+                                    pools=pidx)
     rep.check()
     assert rep.exact >= 0.8 * rep.vectors
     # the pool the screening kernel built equals the oracle's wherever the boundary is clear
-    pidx, psig = parity.pool_from_workspace(ws, T, M, n)
     Af, Xf = to_f64(A), to_f64(X)
     for t in range(T):
         for m in range(M):
@@ -132,6 +135,90 @@ def test_encode_edge_cases():
     rep, _ = parity.compare_encode(A, X[:, 3:4], parity.codes_to_numpy(codes),
                                    parity.oracle_params(p))
     rep.check()
+
+
+@pytest.mark.parametrize("select", ["gm", "pl"])
+@pytest.mark.parametrize("case", [
+    # dtype, d, N, n, s, M, T
+    ("f16", 128, 1000, 64, 1, 70, 2),
+    ("bf16", 64, 513, 32, 2, 65, 2),
+    ("f32", 128, 300, 8, 1, 40, 1),
+    ("bf16", 128, 4096, 256, 2, 64, 2),
+], ids=lambda c: "-".join(map(str, c[:5])))
+def test_encode_parity_sparsity_one_and_two(case, select):
+    """s = 1 (one greedy step, no Gram column) and s = 2 (one column), every row."""
+    dtype, d, N, n, s, M, T = case
+    _banner(f"small s {case} {select}")
+    w = small(dtype, d, N, n, s, M, T=T, aniso=d == 128, s_mix=2)
+    _, A, X = make(w)
+    p = fadkv.Params(n=n, s=s, select=select)
+    ws = fadkv.make_workspace(A.to(DEV), p, M)
+    codes = parity.gpu_encode(A.to(DEV), X.to(DEV), p, workspace=ws)
+    pools, _ = parity.pool_from_workspace(ws, T, M, n)
+    rep, _ = parity.compare_encode(to_f64(A), to_f64(X), parity.codes_to_numpy(codes),
+                                   parity.oracle_params(p), pools=pools)
+    rep.check()
+    assert rep.exact >= 0.85 * rep.vectors
+
+
+@pytest.mark.parametrize("delta", [0.0, float("inf")])
+def test_encode_and_commit_delta_extremes(delta):
+    """delta = 0: every nonzero vector triggers (strictly e > 0) and the commit hands out
+    every inactive atom; delta = +inf: nothing triggers and the commit only counts usage.  The
+    encode is compared row by row and the commit exactly (the oracle committing the GPU's
+    codes)."""
+    _banner(f"delta {delta}")
+    w = Workload("delta", 2, 1, 64, 256, 32, 4, "f16", 1, 96, 4, 0.0, 0.2, None, 41)
+    g = SyntheticKV(w)
+    A = g.atoms()
+    X = g.batch(A, support_limit=160)
+    X[0, 5] = 0                                   # a zero vector never triggers
+    p = fadkv.Params(n=32, s=4, delta_key=delta, delta_value=delta)
+    op = parity.oracle_params(p)
+    At, Xt = A.to(DEV).clone(), X.to(DEV)
+    Ut = torch.zeros(2, 256, dtype=torch.int32, device=DEV)
+    ws = fadkv.make_workspace(At, p, 96)
+    codes = fadkv.fadkv_encode(At, Xt, p, workspace=ws)
+    torch.cuda.synchronize()
+    gpu = parity.codes_to_numpy(codes)
+    pools, _ = parity.pool_from_workspace(ws, 2, 96, 32)
+    rep, _ = parity.compare_encode(to_f64(A), to_f64(X), gpu, op, pools=pools)
+    rep.check()
+    trig = (gpu[3] & FLAG_TRIGGER) != 0
+    if delta == 0.0:
+        assert trig.sum() == 2 * 96 - 1 and not trig[0, 5]
+    else:
+        assert not trig.any()
+    rep_t = fadkv.fadkv_adapt(At, Ut, Xt, codes, p, workspace=ws)
+    torch.cuda.synchronize()
+    nrep, nexh = parity.check_commit(f"delta {delta}", to_f64(A), np.zeros((2, 256), np.int64),
+                                     to_f64(X), gpu, op, "f16", to_f64(At), Ut.cpu().numpy(),
+                                     rep_t.cpu().numpy(), parity.codes_to_numpy(codes))
+    if delta == 0.0:
+        assert nrep > 0 and nexh > 0
+    else:
+        assert nrep == 0 and nexh == 0
+
+
+@pytest.mark.parametrize("select", ["gm", "pl"])
+def test_encode_parity_non_unit_atoms(select):
+    """Atoms of norm 2 to 4 (the library accepts any atoms): scores, pools, the ridge system
+    (whose diagonal is 1.2 ||d_j||^2 + 1e-4) and the residual against the oracle, every row."""
+    _banner(f"non-unit atoms {select}")
+    w = small("f16", 128, 1500, 128, 8, 80, T=2, aniso=True)
+    g = SyntheticKV(w)
+    A = g.atoms().float()
+    rng = np.random.default_rng(6)
+    A = (A * torch.from_numpy(rng.uniform(2.0, 4.0, (2, 1500, 1)).astype(np.float32))).half()
+    X = g.batch(A)
+    p = fadkv.Params(n=128, s=8, select=select)
+    ws = fadkv.make_workspace(A.to(DEV), p, 80)
+    codes = parity.gpu_encode(A.to(DEV), X.to(DEV), p, workspace=ws)
+    pools, _ = parity.pool_from_workspace(ws, 2, 80, 128)
+    rep, _ = parity.compare_encode(to_f64(A), to_f64(X), parity.codes_to_numpy(codes),
+                                   parity.oracle_params(p), pools=pools)
+    rep.check()
+    assert rep.exact >= 0.85 * rep.vectors
 
 
 def test_select_is_bounded_for_any_pool_and_non_finite_atoms():
@@ -284,8 +371,12 @@ def test_adapt_parity_both_commit_paths():
 
 
 def test_encode_adapt_multistep_parity():
-    """Eight steps of 64 vectors (supports from atoms [0,192), 20% Gaussian rows): the GPU
-    state (atoms, usage) and the oracle's evolve independently and agree step by step."""
+    """Eight steps of 64 vectors (supports from atoms [0,192), 20% Gaussian rows).  Every step
+    starts the oracle from the GPU's state (atoms, usage): the encode is compared row by row
+    (near-ties replayed inside the GPU's own pools) and the commit exactly, the oracle
+    committing the GPU's codes.  So every step is checked strictly, the late ones included,
+    whatever near-ties earlier steps met.  The oracle's own evolution is followed alongside
+    and must agree with the GPU's for as long as neither met a near-tie decision."""
     _banner("multistep")
     w = Workload("steps", 1, 1, 64, 256, 32, 4, "f32", 1, 64, 4, 0.0, 0.2, None, 21)
     g = SyntheticKV(w)
@@ -294,31 +385,36 @@ def test_encode_adapt_multistep_parity():
     op = parity.oracle_params(p)
     At = A0.to(DEV).clone()
     Ut = torch.zeros(1, 256, dtype=torch.int32, device=DEV)
-    Ao, Uo = to_f64(A0), np.zeros((1, 256), np.int64)
-    strict_steps = 0
+    ws = fadkv.make_workspace(At, p, 64)
+    Ao, Uo = to_f64(A0), np.zeros((1, 256), np.int64)      # the oracle's own evolution
+    same_evolution = True
+    replaced_total = 0
     for step in range(8):
         X = g.batch(A0, step=step, support_limit=192)
-        Xt = X.to(DEV)
-        codes = fadkv.fadkv_encode(At, Xt, p)
+        Xt, Xf = X.to(DEV), to_f64(X)
+        A_b, U_b = to_f64(At), Ut.cpu().numpy().astype(np.int64)
+        codes = fadkv.fadkv_encode(At, Xt, p, workspace=ws)
         torch.cuda.synchronize()
         gpu = parity.codes_to_numpy(codes)
-        rep_enc, oc = parity.compare_encode(Ao, to_f64(X), gpu, op)
+        pools, _ = parity.pool_from_workspace(ws, 1, 64, 32)
+        rep_enc, oc = parity.compare_encode(A_b, Xf, gpu, op, pools=pools)
         rep_enc.check()
-        grep = fadkv.fadkv_adapt(At, Ut, Xt, codes, p)
+        grep = fadkv.fadkv_adapt(At, Ut, Xt, codes, p, workspace=ws)
         torch.cuda.synchronize()
-        Ao, Uo, ncodes, orep = oracle.adapt(Ao, Uo, to_f64(X), oc, op, "f32")
-        # adaptation consumes only the supports and trigger bits: where both sides agree on
-        # those (near-ties included) the commit must agree exactly; otherwise the two states
-        # may legitimately part
-        if not (np.array_equal(gpu[0], oc.idx) and
-                np.array_equal(gpu[3] & FLAG_TRIGGER, oc.flags & FLAG_TRIGGER)):
-            break
-        np.testing.assert_array_equal(grep.cpu().numpy(), orep)
-        np.testing.assert_array_equal(Ut.cpu().numpy(), Uo)
-        np.testing.assert_array_equal(to_f64(At), Ao)
+        nrep, _ = parity.check_commit(f"step {step}", A_b, U_b, Xf, gpu, op, "f32", to_f64(At),
+                                      Ut.cpu().numpy(), grep.cpu().numpy(),
+                                      parity.codes_to_numpy(codes))
+        replaced_total += nrep
+        if same_evolution:
+            Ao, Uo, _, orep = oracle.adapt(Ao, Uo, Xf, oc, op, "f32")
+            if int(oc.ties.max()) == 0:
+                np.testing.assert_array_equal(grep.cpu().numpy(), orep)
+                np.testing.assert_array_equal(Ut.cpu().numpy(), Uo)
+                np.testing.assert_array_equal(to_f64(At), Ao)
+            else:
+                same_evolution = False
         assert At.shape == A0.shape
-        strict_steps += 1
-    assert strict_steps >= 4
+    assert replaced_total > 0
 
 
 # ------------------------------------------------------------------------------------------
@@ -387,8 +483,9 @@ def test_append_parity_capacity_exhaustion():
 
 def test_encode_append_multistep_parity():
     """Eight steps of 64 vectors on two dictionaries that start with 128 and 160 of 256 slots in
-    use: GPU encode + append and the oracle's evolve independently and agree step by step while
-    both sides agree on the supports and trigger bits."""
+    use.  Each step starts the oracle from the GPU's state (atoms, usage, n_atoms): the encode
+    is compared row by row and the append commit exactly, the oracle committing the GPU's
+    codes, on every step."""
     _banner("append multistep")
     w = Workload("steps", 2, 1, 64, 256, 32, 4, "f32", 1, 64, 4, 0.0, 0.2, None, 23)
     g = SyntheticKV(w)
@@ -399,29 +496,29 @@ def test_encode_append_multistep_parity():
     At = A0.to(DEV).clone()
     Ut = torch.zeros(2, 256, dtype=torch.int32, device=DEV)
     Nt = torch.tensor(n_start, dtype=torch.int32, device=DEV)
-    Ao, Uo, No = to_f64(A0), np.zeros((2, 256), np.int64), np.array(n_start)
-    strict_steps = 0
+    ws = fadkv.make_workspace(At, p, 64)
     for step in range(8):
         X = g.batch(A0, step=step, support_limit=128)
-        Xt = X.to(DEV)
-        codes = fadkv.fadkv_encode(At, Xt, p)
+        Xt, Xf = X.to(DEV), to_f64(X)
+        A_b, U_b, N_b = to_f64(At), Ut.cpu().numpy().astype(np.int64), Nt.cpu().numpy()
+        codes = fadkv.fadkv_encode(At, Xt, p, workspace=ws)
         torch.cuda.synchronize()
         gpu = parity.codes_to_numpy(codes)
-        rep_enc, oc = parity.compare_encode(Ao, to_f64(X), gpu, op)
+        pools, _ = parity.pool_from_workspace(ws, 2, 64, 32)
+        rep_enc, _ = parity.compare_encode(A_b, Xf, gpu, op, pools=pools)
         rep_enc.check()
-        grep = fadkv.fadkv_adapt_append(At, Ut, Xt, codes, p, Nt)
+        grep = fadkv.fadkv_adapt_append(At, Ut, Xt, codes, p, Nt, workspace=ws)
         torch.cuda.synchronize()
-        Ao, Uo, _, orep, No = oracle.append(Ao, Uo, to_f64(X), oc, No, op, "f32")
-        if not (np.array_equal(gpu[0], oc.idx) and
-                np.array_equal(gpu[3] & FLAG_TRIGGER, oc.flags & FLAG_TRIGGER)):
-            break
+        na, nu, ncodes, orep, nn = oracle.append(A_b, U_b, Xf, parity.gpu_codes_as_oracle(*gpu),
+                                                 N_b, op, "f32")
         np.testing.assert_array_equal(grep.cpu().numpy(), orep)
-        np.testing.assert_array_equal(Nt.cpu().numpy(), No)
-        np.testing.assert_array_equal(Ut.cpu().numpy(), Uo)
-        np.testing.assert_array_equal(to_f64(At), Ao)
-        strict_steps += 1
-    assert strict_steps >= 4
-    assert np.all(No > np.array(n_start))
+        np.testing.assert_array_equal(Nt.cpu().numpy(), np.minimum(nn, 256))
+        np.testing.assert_array_equal(Ut.cpu().numpy(), nu)
+        np.testing.assert_array_equal(to_f64(At), na)
+        gi, gc, ge, gf = parity.codes_to_numpy(codes)
+        np.testing.assert_array_equal(gi, ncodes.idx)
+        np.testing.assert_array_equal(gf, ncodes.flags)
+    assert np.all(Nt.cpu().numpy() > np.array(n_start))
 
 
 # ------------------------------------------------------------------------------------------
@@ -458,7 +555,12 @@ def _sample_rows(T, M, count, seed):
     return sorted(set(zip(ts.tolist(), ms.tolist())))
 
 
-def _full_size(name, samples, steps=1, select="gm"):
+def _full_size(name, samples, steps=1, select="gm", commit_dicts=(0, 1)):
+    """Encode (and commit) full-size steps of a workload in the benchmark's launch
+    configuration.  Sampled rows are compared with the oracle one vector at a time (near-ties
+    replayed inside the GPU's own pools), at least 85 % of them exactly; the commit of
+    `commit_dicts` (a key and a value dictionary) is compared exactly, the oracle committing
+    the GPU's own codes of every row of those dictionaries from the GPU's step-start state."""
     w = synth.WORKLOADS[name]
     _banner(f"full size {name} ({select}): {w.num_dicts} dicts x {w.M} vectors")
     g = SyntheticKV(w, device=DEV)
@@ -467,13 +569,16 @@ def _full_size(name, samples, steps=1, select="gm"):
     p = fadkv.Params(n=w.n, s=w.s, select=select)
     ws = fadkv.make_workspace(A, p, w.M)
     op = parity.oracle_params(p)
+    cd = list(commit_dicts)
     for step in range(steps):
         X = g.batch(A, step=step)
         A_before = to_f64(A)
+        U_before = U.cpu().numpy().astype(np.int64)
         codes = fadkv.fadkv_encode(A, X, p, workspace=ws)
         torch.cuda.synchronize()
         gi, gc, ge, gf = parity.codes_to_numpy(codes)
         rows = _sample_rows(w.num_dicts, w.M, samples, seed=step)
+        pools = parity.pool_rows_from_workspace(ws, w.num_dicts, w.M, w.n, rows)
         Xf = {}
         for (t, m) in rows:
             Xf[(t, m)] = X[t, m].float().cpu().double().numpy()
@@ -483,13 +588,15 @@ def _full_size(name, samples, steps=1, select="gm"):
             oc = oracle.encode_vector(A_before[t], Xf[(t, m)], op, delta)
             parity.compare_vector(rep, f"{name} step {step} dict {t} row {m}", A_before[t],
                                   Xf[(t, m)], gi[t, m], gc[t, m], ge[t, m], int(gf[t, m]), oc,
-                                  op, delta)
+                                  op, delta, pool=pools[(t, m)])
         rep.check()
+        assert rep.exact >= 0.85 * (rep.vectors - rep.nonfinite), \
+            f"only {rep.exact} of {rep.vectors} sampled rows compared exactly"
         trig_before = (gf & FLAG_TRIGGER) != 0
         used_before = U.sum().item()
         rep_t = fadkv.fadkv_adapt(A, U, X, codes, p, workspace=ws)
         torch.cuda.synchronize()
-        _, _, _, gf2 = parity.codes_to_numpy(codes)
+        gi2, gc2, ge2, gf2 = parity.codes_to_numpy(codes)
         replaced = rep_t.cpu().numpy()
         assert A.shape == (w.num_dicts, w.N, w.d)            # the dictionary never grows
         assert np.all((replaced >= 0) == ((gf2 & FLAG_REPLACED) != 0))
@@ -498,8 +605,14 @@ def _full_size(name, samples, steps=1, select="gm"):
             r = replaced[t][replaced[t] >= 0]
             assert len(set(r.tolist())) == r.size
         assert U.sum().item() >= used_before
-        _banner(f"  step {step}: {rep.vectors} sampled rows ({rep.near_tie} near-tie), "
-                f"{int(trig_before.sum())} triggers, {int((replaced >= 0).sum())} replaced")
+        nrep, nexh = parity.check_commit(
+            f"{name} step {step} dicts {cd}", A_before[cd], U_before[cd], to_f64(X[cd]),
+            (gi[cd], gc[cd], ge[cd], gf[cd]), op, w.dtype, to_f64(A[cd]),
+            U[cd].cpu().numpy(), replaced[cd], (gi2[cd], gc2[cd], ge2[cd], gf2[cd]))
+        _banner(f"  step {step}: {rep.vectors} sampled rows ({rep.exact} exact, "
+                f"{rep.near_tie} near-tie), {int(trig_before.sum())} triggers, "
+                f"{int((replaced >= 0).sum())} replaced; commit of dicts {cd} exact "
+                f"({nrep} replaced, {nexh} exhausted)")
 
 
 def test_full_size_llama3b_decode_sampled():
