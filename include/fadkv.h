@@ -61,7 +61,9 @@ typedef enum {
   FADKV_ERR_DTYPE = -2,     /* unsupported dtype code */
   FADKV_ERR_SHAPE = -3,     /* d, N, n, s or M outside the limits above */
   FADKV_ERR_WORKSPACE = -4, /* workspace null or smaller than fadkv_workspace_bytes */
-  FADKV_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed */
+  FADKV_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed */
+  FADKV_ERR_SCRATCH = -6    /* fadkv_encode_noalloc: the call needs more than its static
+                               scratch (FADKV_NOALLOC_SCRATCH_BYTES) */
 } fadkv_status;
 
 typedef enum { FADKV_F32 = 0, FADKV_F16 = 1, FADKV_BF16 = 2 } fadkv_dtype;
@@ -120,6 +122,24 @@ int fadkv_workspace_bytes(const fadkv_dict *dict, const fadkv_params *params, in
 int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void *X, int64_t M,
                  const fadkv_codes *out, void *workspace, size_t workspace_bytes,
                  hipStream_t stream);
+
+/* fadkv_encode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and the same
+ * results as fadkv_encode, with the candidate pools kept in a static device array of
+ * FADKV_NOALLOC_SCRATCH_BYTES instead of a caller workspace.  Each GPU the library runs on
+ * holds its own copy of that array until the process ends; the call uses the copy of the
+ * current device (make the device of `stream` current before calling).  It allocates
+ * nothing, enqueues no memset and never synchronises.
+ *   Limit: the call needs fadkv_workspace_bytes(dict, params, M) <= FADKV_NOALLOC_SCRATCH_BYTES
+ *   (about num_dicts * M * (6 n + 1) bytes; e.g. 56 x 256 vectors at n = 256, or 64 x 512 at
+ *   n = 512); larger calls return FADKV_ERR_SCRATCH and launch nothing.
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls that overlap on one
+ *   GPU (two streams, two host threads) race; serialise them (one stream) or use fadkv_encode
+ *   with separate workspaces.  The array keeps the last call's contents; nothing in it needs
+ *   to start at zero. */
+#define FADKV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int fadkv_encode_noalloc(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                         int64_t M, const fadkv_codes *out, hipStream_t stream);
 
 /* The two stages of fadkv_encode, for callers that want the candidate pool itself (e.g. to
  * measure how much of a full pursuit's support it recalls, Figure 1b) or to time each stage.

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -125,6 +127,29 @@ hipError_t run_select(const fadkv_dict *dict, const fadkv_params *p, const void 
                               out->relerr, out->flags, stream);
 }
 
+// ---- static scratch of fadkv_encode_noalloc ---------------------------------------------------
+// The array's name is only a host-side stand-in in host code: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address
+// is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[FADKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once taken
+
+int scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FADKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FADKV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FADKV_OK;
+}
+
 #define FADKV_TRY(expr)        \
   do {                         \
     const int _st = (expr);    \
@@ -145,6 +170,8 @@ const char *fadkv_status_string(int status) {
     case FADKV_ERR_SHAPE: return "shape outside the supported limits";
     case FADKV_ERR_WORKSPACE: return "workspace missing or too small";
     case FADKV_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case FADKV_ERR_SCRATCH:
+      return "fadkv_encode_noalloc needs more than its static scratch (FADKV_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -176,6 +203,30 @@ int fadkv_encode(const fadkv_dict *dict, const fadkv_params *params, const void 
     return FADKV_ERR_WORKSPACE;
   if (M == 0) return FADKV_OK;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
+  uint16_t *pool_idx = reinterpret_cast<uint16_t *>(ws + L.pool_idx);
+  float *pool_sig = reinterpret_cast<float *>(ws + L.pool_sig);
+  uint8_t *vstat = ws + L.vstat;
+  if (fadkv::launch_score_topn(dict->dtype, dict->d, dict->atoms, X, dict->num_dicts, dict->N,
+                               (int)M, params->n, pool_idx, pool_sig, vstat, stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  if (run_select(dict, params, X, M, pool_idx, pool_sig, vstat, out, stream) != hipSuccess)
+    return FADKV_ERR_HIP;
+  return FADKV_OK;
+}
+
+int fadkv_encode_noalloc(const fadkv_dict *dict, const fadkv_params *params, const void *X,
+                         int64_t M, const fadkv_codes *out, hipStream_t stream) {
+  FADKV_TRY(check_dict(dict));
+  FADKV_TRY(check_params(dict, params));
+  FADKV_TRY(check_M(dict, M));
+  FADKV_TRY(check_codes(out));
+  if (M > 0 && (!X || !aligned(X, 16))) return FADKV_ERR_ARG;
+  const Layout L = layout(dict, params, M);
+  if (L.encode_end > FADKV_NOALLOC_SCRATCH_BYTES) return FADKV_ERR_SCRATCH;
+  if (M == 0) return FADKV_OK;
+  void *ptr = nullptr;
+  FADKV_TRY(scratch_of_current_device(&ptr));
+  uint8_t *ws = static_cast<uint8_t *>(ptr);
   uint16_t *pool_idx = reinterpret_cast<uint16_t *>(ws + L.pool_idx);
   float *pool_sig = reinterpret_cast<float *>(ws + L.pool_sig);
   uint8_t *vstat = ws + L.vstat;

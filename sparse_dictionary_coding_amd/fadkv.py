@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
         h.fadkv_encode.restype = ctypes.c_int
         h.fadkv_encode.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p, ctypes.c_int64,
                                    P(fadkv_codes), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        h.fadkv_encode_noalloc.restype = ctypes.c_int
+        h.fadkv_encode_noalloc.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p,
+                                           ctypes.c_int64, P(fadkv_codes), ctypes.c_void_p]
         h.fadkv_screen.restype = ctypes.c_int
         h.fadkv_screen.argtypes = [P(fadkv_dict), P(fadkv_params), ctypes.c_void_p, ctypes.c_int64,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -223,6 +226,30 @@ def fadkv_encode(atoms: torch.Tensor, X: torch.Tensor, params: Params,
                             _stream(stream))
     if st != FADKV_OK:
         raise FadkvError("fadkv_encode", st)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20    # FADKV_NOALLOC_SCRATCH_BYTES
+FADKV_ERR_SCRATCH = -6
+
+
+def fadkv_encode_noalloc(atoms: torch.Tensor, X: torch.Tensor, params: Params,
+                         out: Optional[Codes] = None, stream=None) -> Codes:
+    """fadkv_encode with the library's static per-GPU scratch instead of a workspace (for
+    callers that cannot allocate); `out` is the caller's, allocated here only when not given.
+    Calls that overlap on one GPU race on that scratch."""
+    dd = _dict(atoms)
+    T, N, d = atoms.shape
+    _check(X, "X", atoms.dtype)
+    if X.dim() != 3 or X.shape[0] != T or X.shape[2] != d:
+        raise ValueError(f"X must be [{T}][M][{d}]")
+    M = X.shape[1]
+    if out is None:
+        out = Codes.empty(T, M, params.s, atoms.device)
+    st = lib().fadkv_encode_noalloc(ctypes.byref(dd), ctypes.byref(params.c()), X.data_ptr(), M,
+                                    ctypes.byref(out.c()), _stream(stream))
+    if st != FADKV_OK:
+        raise FadkvError("fadkv_encode_noalloc", st)
     return out
 
 

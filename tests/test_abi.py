@@ -250,3 +250,22 @@ def test_size_limits_at_the_boundary():
     assert att((1 << 22) + 1, 1) == -3 and att((1 << 18) + 1, 64) == -3
     assert att(1 << 18, 64) == -4        # accepted shape; only the tiny workspace is refused
 
+
+def test_encode_noalloc_argument_and_scratch_checks():
+    """fadkv_encode_noalloc refuses, before touching the GPU, a call whose pools exceed its
+    static scratch (FADKV_ERR_SCRATCH) and bad arguments as fadkv_encode does."""
+    L = fadkv.lib()
+    codes = _codes()
+
+    def enc(dd, pp, M, X=FAKE):
+        return L.fadkv_encode_noalloc(ctypes.byref(dd), ctypes.byref(pp), X, M,
+                                      ctypes.byref(codes), None)
+    dd, pp = _dict(num_dicts=56, N=4096), _params()
+    st, need = _ws(dd, pp, 256)
+    assert st == 0 and need <= fadkv.NOALLOC_SCRATCH_BYTES      # the 3B decode step fits
+    assert enc(dd, pp, 2000) == fadkv.FADKV_ERR_SCRATCH
+    assert enc(dd, pp, 10, X=FAKE + 8) == -1
+    assert enc(_dict(d=96), pp, 10) == -3
+    assert enc(dd, _params(n=4), 10) == -3
+    assert enc(dd, pp, 0) == 0
+    assert fadkv.fadkv_status_string(fadkv.FADKV_ERR_SCRATCH) != "unknown status"
