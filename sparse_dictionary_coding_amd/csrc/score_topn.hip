@@ -234,7 +234,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void score_topn_kernel(
     const uint8_t *__restrict__ atoms, const uint8_t *__restrict__ X, int num_dicts, int N, int M,
     int n, uint16_t *__restrict__ pool_idx, float *__restrict__ pool_sig,
-    uint8_t *__restrict__ vstat) {
+    uint8_t *__restrict__ vstat, unsigned base) {
   using G = Geo<DT, D>;
   __shared__ __attribute__((aligned(16))) uint4 s_stage[WAVES * G::STAGE];
   __shared__ uint32_t s_reg[VT * REGW];
@@ -244,12 +244,16 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
   __shared__ int s_busy;
   __shared__ uint2 s_queue[WAVES * QCAP];
 
-  // workgroup i runs on XCD i % 8; its r-th workgroup takes dictionary x + 8 * (r / B)
-  const int nvb = (M + VT - 1) / VT;
-  const int xcd = blockIdx.x % 8, rr = blockIdx.x / 8;
-  const int dict = xcd + 8 * (rr / nvb);
+  // workgroup i runs on XCD i % 8; its r-th workgroup takes dictionary x + 8 * (r / B).
+  // (32-bit arithmetic: fewer than 2^31 workgroups over all chunks; base is a multiple of 8,
+  // so the XCD of workgroup bid is still bid % 8)
+  const unsigned bid = base + blockIdx.x;
+  const unsigned nvb = (unsigned)(((size_t)M + VT - 1) / VT);
+  const int xcd = (int)(bid % 8u);
+  const unsigned rr = bid / 8u;
+  const int dict = xcd + 8 * (int)(rr / nvb);
   if (dict >= num_dicts) return;
-  const int v0 = (rr % nvb) * VT;
+  const int v0 = (int)(rr % nvb) * VT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint8_t *dict_atoms = atoms + (size_t)dict * N * G::ROWB;
@@ -502,7 +506,8 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
 
 #define FADKV_SCORE_INST(DT, D)                                                                   \
   template __global__ void score_topn_kernel<DT, D>(const uint8_t *, const uint8_t *, int, int,  \
-                                                    int, int, uint16_t *, float *, uint8_t *);
+                                                    int, int, uint16_t *, float *, uint8_t *,    \
+                                                    unsigned);
 FADKV_SCORE_INST(DT_F32, 64)
 FADKV_SCORE_INST(DT_F32, 128)
 FADKV_SCORE_INST(DT_F16, 64)
@@ -513,17 +518,23 @@ FADKV_SCORE_INST(DT_BF16, 128)
 hipError_t launch_score_topn(int dtype, int d, const void *atoms, const void *X, int num_dicts,
                              int N, int M, int n, uint16_t *pool_idx, float *pool_sig,
                              uint8_t *vstat, hipStream_t stream) {
-  const int nvb = (M + VT - 1) / VT;
-  dim3 grid((unsigned)(8 * ((num_dicts + 7) / 8) * nvb)), block(THREADS);
+  const size_t nvb = ((size_t)M + VT - 1) / VT;
+  // num_dicts * M < 2^31 vectors: fewer than 2^31 workgroups; launched in chunks of at most
+  // kMaxBlocksPerLaunch (a multiple of 8, so every chunk keeps the XCD numbering)
+  const size_t total = 8 * (((size_t)num_dicts + 7) / 8) * nvb;
   const uint8_t *A = static_cast<const uint8_t *>(atoms);
   const uint8_t *Xb = static_cast<const uint8_t *>(X);
+  for (size_t b0 = 0; b0 < total; b0 += kMaxBlocksPerLaunch) {
+    const size_t nb = total - b0 < kMaxBlocksPerLaunch ? total - b0 : kMaxBlocksPerLaunch;
+    const dim3 grid((unsigned)nb), block(THREADS);
 #define L(DT, D)                                                                              \
   hipLaunchKernelGGL((score_topn_kernel<DT, D>), grid, block, 0, stream, A, Xb, num_dicts, N, M, \
-                     n, pool_idx, pool_sig, vstat)
-  if (dtype == DT_F32) { if (d == 64) L(DT_F32, 64); else L(DT_F32, 128); }
-  else if (dtype == DT_F16) { if (d == 64) L(DT_F16, 64); else L(DT_F16, 128); }
-  else { if (d == 64) L(DT_BF16, 64); else L(DT_BF16, 128); }
+                     n, pool_idx, pool_sig, vstat, (unsigned)b0)
+    if (dtype == DT_F32) { if (d == 64) L(DT_F32, 64); else L(DT_F32, 128); }
+    else if (dtype == DT_F16) { if (d == 64) L(DT_F16, 64); else L(DT_F16, 128); }
+    else { if (d == 64) L(DT_BF16, 64); else L(DT_BF16, 128); }
 #undef L
+  }
   return hipGetLastError();
 }
 
