@@ -60,7 +60,7 @@ struct VecState {           // one of the lane's two vectors during one sweep
   int vi;                   // vector within the workgroup
   int base;                 // level-0: key >> 18 of bin 0
   int off;                  // level-0: region word of (key >> 18) is (key >> 18) + off
-  uint32_t lo32, hi32;      // boundary bin in 31-bit key space (level 0)
+  uint32_t lo32, hi32;      // boundary bin in 31-bit key space (level 0); lo32 = 2^32 - 1: no hit
   u64 lo, hi;               // boundary range in composite-key space (refinement)
   int shift;
   uint16_t *pidx;
@@ -156,7 +156,7 @@ __device__ __forceinline__ void collect_tile(const float4_t &acc0, const float4_
   for (int b = 0; b < 8; ++b) {
     const VecState &q = vs[b >> 2];
     const uint32_t key = __float_as_uint(v[b]) & 0x7fffffffu;
-    const bool ok = q.active && (!CHECK || atom0 + (b & 3) < N);
+    const bool ok = !CHECK || atom0 + (b & 3) < N;
     m |= (ok && key >= q.lo32) ? 1u << b : 0u;
   }
   for (;;) {
@@ -388,7 +388,9 @@ __global__ __launch_bounds__(THREADS, (DT == DT_F32 && D == 128) ? 1 : 4) void s
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     vs[k].active = s_state[vs[k].vi] == ST_COLLECT;
-    vs[k].lo32 = s_lo32[vs[k].vi];
+    // a vector that does not collect gets a bound no 31-bit key reaches, so the collect pass
+    // needs no per-slot activity test
+    vs[k].lo32 = vs[k].active ? s_lo32[vs[k].vi] : 0xFFFFFFFFu;
     vs[k].hi32 = s_hi32[vs[k].vi];
   }
   sweep<DT, D, PASS_COLLECT, true>(dict_atoms, N, n, wave, lane, b, vs, sh, stage, stage_lds, ring);
